@@ -1,0 +1,277 @@
+"""Benchmark of the W4A16 MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one synthetic batch: routing
+alignment (chord_moe_align) and the layer (tile build, gate_up GEMM + SiLU*mul,
+down GEMM, weighted combine) for the indexed layout; the layer alone for the
+grouped layouts (their row maps are the dispatcher's output).  Inputs are
+resident in HBM before the timed region.  Weight replicas are rotated across
+steps so that every step streams its weights from HBM, not from the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line (rank 0).  `roofline` reports the dominant kernel
+(gate_up for decode-shaped calls, the bigger of the two GEMMs otherwise)
+against HBM (8 TB/s) or dense BF16 MFMA (2.5 PFLOP/s) from its algorithmic
+bytes / FLOPs and its average duration, measured with HIP events recorded by
+the library on the launch stream over the timed region.  `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("W4A16 MoE layer µs/call + achieved HBM TB/s (decode) / MFMA TFLOPS (prefill)")
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+W_BYTES = 0.5625          # one packed nibble + a bf16 scale per 32 weights
+DEFAULT_WORKLOAD = "kimi_decode_T64_ep48of384_top8"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one call (from the actual routing draw)
+# ---------------------------------------------------------------------------
+
+def algorithmic_work(wl):
+    """Per-stage algorithmic HBM bytes and FLOPs of one layer call.
+
+    Weights: each active expert's packed codes and scales read once
+    (0.5625 B/weight).  gate_up also reads each routed token row once (for the
+    indexed layout: each token with a local slot) and writes h (2 B x I per
+    routed row); down reads h and writes y / output rows (2 B x H per routed
+    row).  FLOPs count valid rows only: 2*R*H*2I (gate_up) + 2*R*I*H (down).
+    """
+    H, I = wl.H, wl.I
+    if wl.layout == "masked":
+        counts = np.asarray(wl.masked_m, dtype=np.int64)
+        R = int(counts.sum())
+        T_u = R
+    else:
+        ids = wl.topk_ids - wl.expert_begin
+        local = (ids >= 0) & (ids < wl.E_l)
+        counts = np.bincount(ids[local], minlength=wl.E_l)
+        R = int(local.sum())
+        T_u = int(np.any(local, axis=1).sum())
+    active = int((counts > 0).sum())
+    w13 = active * 2 * I * H * W_BYTES
+    w2 = active * H * I * W_BYTES
+    gu_bytes = w13 + 2 * H * T_u + 2 * I * R
+    dn_bytes = w2 + 2 * I * R + 2 * H * R
+    gu_flops = 2.0 * R * H * 2 * I
+    dn_flops = 2.0 * R * I * H
+    return dict(R=R, T_u=T_u, active=active, gate_up_bytes=gu_bytes, down_bytes=dn_bytes,
+                gate_up_flops=gu_flops, down_flops=dn_flops,
+                layer_bytes=w13 + w2 + 2 * H * T_u + 4 * I * R + 2 * H * (wl.T or R),
+                layer_flops=gu_flops + dn_flops)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, budget_s):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    if wl.layout == "masked":
+        order = [e for e in np.argsort(-wl.masked_m) if wl.masked_m[e] > 0]
+        done_rows, t0 = 0, time.perf_counter()
+        n_e = 0
+        for e in order:
+            m = int(wl.masked_m[e])
+            oracle.grouped_masked(wl.a3[e:e + 1, :m], np.array([m], np.int32), wl.q13[e:e + 1],
+                                  wl.s13[e:e + 1], wl.q2[e:e + 1], wl.s2[e:e + 1])
+            done_rows += m
+            n_e += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+        total = int(wl.masked_m.sum())
+        scale = total / max(done_rows, 1)
+        sample = f"oracle on {n_e} of {int((wl.masked_m > 0).sum())} active experts " \
+                 f"({done_rows} of {total} rows), scaled by rows"
+    else:
+        ids = wl.topk_ids - wl.expert_begin
+        local = (ids >= 0) & (ids < wl.E_l)
+        tokens = np.nonzero(np.any(local, axis=1))[0]
+        rng = np.random.default_rng(0)
+        order = rng.permutation(tokens)
+        done, slots, t0 = [], 0, time.perf_counter()
+        step = 1
+        while len(done) < len(order):
+            batch = order[len(done):len(done) + step]
+            oracle.moe_layer(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2,
+                             wl.expert_begin, tokens=batch)
+            done.extend(batch.tolist())
+            slots += int(local[batch].sum())
+            if time.perf_counter() - t0 > budget_s:
+                break
+            step = min(step * 2, 64)
+        el = time.perf_counter() - t0
+        total = int(local.sum())
+        scale = total / max(slots, 1)
+        sample = f"oracle on {len(done)} of {len(tokens)} tokens with a local slot " \
+                 f"({slots} of {total} routed slots), scaled by slots"
+    return {"value": el * scale * 1e6, "unit": "us/call", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "measured_s": round(el, 3)}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N>1 is not supported "
+                                   "(the layer takes one GPU's expert share, no collectives)"}))
+        sys.exit(2)
+    import torch
+    from moe_inputs import gen as G
+    from moe_inputs.configs import workload_by_name
+    from quantized_moe_amd import chord as C
+    from quantized_moe_amd.moe import W4A16MoE
+
+    spec = workload_by_name(args.workload)
+    wl = G.make_workload(spec)
+    dev = torch.device("cuda:0")
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def dbf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    mode = {"indexed": C.MODE_INDEXED, "contiguous": C.MODE_CONTIGUOUS,
+            "masked": C.MODE_MASKED}[wl.layout]
+    weight_bytes = (wl.q13.nbytes + wl.q2.nbytes) * 9 // 8
+    n_rep = 2 if weight_bytes > 300e6 else int(math.ceil(600e6 / weight_bytes)) + 1
+    q13, s13, q2, s2 = d(wl.q13), dbf(wl.s13), d(wl.q2), dbf(wl.s2)
+    layers = [W4A16MoE(q13, s13, q2, s2, mode=mode) for _ in range(n_rep)]
+    del q13, s13, q2, s2
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    if wl.layout == "indexed":
+        x, ids, w = dbf(wl.x), d(wl.topk_ids), d(wl.topk_weights)
+        bm = C.chord_w4a16_moe_indexed_block_m(wl.T, wl.k, wl.E_g, wl.E_l, wl.H, wl.I)
+        mp = C.chord_moe_align_max_padded(wl.T, wl.k, wl.E_l, bm)
+        al_out = (torch.empty(mp, dtype=torch.int32, device=dev),
+                  torch.empty((mp + bm - 1) // bm, dtype=torch.int32, device=dev),
+                  torch.empty(1, dtype=torch.int32, device=dev))
+        al_ws = torch.empty(max(1, C.lib.chord_moe_align_workspace_bytes(wl.T, wl.k, wl.E_l, bm)),
+                            dtype=torch.uint8, device=dev)
+        out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        for L in layers:
+            L.workspace(C.chord_w4a16_moe_workspace_bytes(C.MODE_INDEXED, wl.T, wl.k, wl.E_l, wl.H,
+                                                          wl.I, mp), dev)
+
+        def step(i):
+            L = layers[i % n_rep]
+            C.chord_moe_align(ids, wl.expert_begin, wl.E_l, bm, max_padded=mp, out=al_out,
+                              workspace=al_ws)
+            L.indexed(x, ids, w, wl.expert_begin, wl.E_g, align=(*al_out, bm), out=out)
+        config = {"workload": spec.name, "layout": "indexed", "T": wl.T, "H": wl.H, "I": wl.I,
+                  "E_global": wl.E_g, "E_local": wl.E_l, "top_k": wl.k, "block_m": bm}
+    elif wl.layout == "contiguous":
+        a, m_idx, f2r, nvalid = G.build_contiguous(wl.topk_ids, wl.x, wl.expert_begin, wl.E_l)
+        a_d, m_d = dbf(a), d(m_idx)
+        out_rows = torch.empty((a.shape[0], wl.H), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            layers[i % n_rep].contiguous(a_d, m_d, nvalid, out_rows=out_rows)
+        config = {"workload": spec.name, "layout": "contiguous", "T": wl.T, "M": int(a.shape[0]),
+                  "H": wl.H, "I": wl.I, "E_local": wl.E_l, "top_k": wl.k}
+    else:
+        a3, mm = dbf(wl.a3), d(wl.masked_m)
+        out = torch.empty((wl.E_l * wl.max_m, wl.H), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            layers[i % n_rep].masked(a3, mm, wl.expected_m, out=out)
+        config = {"workload": spec.name, "layout": "masked", "E_local": wl.E_l, "max_m": wl.max_m,
+                  "H": wl.H, "I": wl.I, "expected_m": wl.expected_m,
+                  "rows": int(wl.masked_m.sum())}
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan = C.last_plan()
+
+    C.chord_profile_reset()
+    C.chord_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    C.chord_profile_enable(False)
+    stage_ms, calls = C.chord_profile_read()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    work = algorithmic_work(wl)
+    avg = [m / max(calls, 1) for m in stage_ms]           # ms per call per stage
+    gu_ms, dn_ms = avg[1], avg[2]
+    decode_shaped = work["layer_flops"] / max(work["layer_bytes"], 1) < 2.5e15 / 8e12
+    if decode_shaped:
+        name, dur, alg, = "gate_up", gu_ms, work["gate_up_bytes"]
+        if dn_ms > gu_ms:
+            name, dur, alg = "down", dn_ms, work["down_bytes"]
+        achieved = alg / (dur * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes": int(alg), "avg_ms": round(dur, 5)}
+    else:
+        name, dur, alg = "gate_up", gu_ms, work["gate_up_flops"]
+        if dn_ms > gu_ms:
+            name, dur, alg = "down", dn_ms, work["down_flops"]
+        achieved = alg / (dur * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops": alg, "avg_ms": round(dur, 5)}
+    layer_ms = sum(avg)
+    extra = {"stage_ms": [round(m, 5) for m in avg], "layer_kernels_ms": round(layer_ms, 5),
+             "layer_hbm_GBs": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+             "layer_TFLOPs": round(work["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+             "routed_rows": work["R"], "active_experts": work["active"], "plan": plan,
+             "weight_replicas": n_rep}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    line = {"metric": METRIC, "value": round(ms_per_step * 1e3, 2), "unit": "us/call",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 5), "higher_is_better": False, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": config, "roofline": roof, "cpu_baseline": cpu, "detail": extra}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

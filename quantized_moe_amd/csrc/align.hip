@@ -1,0 +1,205 @@
+// Routing alignment for the indexed layer: a stable counting sort of the flat
+// (token, slot) ids by local expert, each expert's group padded to a multiple
+// of block_m with the sentinel T*k, plus the per-block expert ids and the
+// padded total.  Ranks inside a group come from wavefront ballots (a 10-bit
+// match of the expert id) and per-wave counts in LDS, so the order is the
+// ascending flat index and the result is deterministic.
+//
+// Small inputs (<= kAlignChunk entries) run in one workgroup; larger ones in
+// three launches: per-chunk histograms, one offsets workgroup, per-chunk
+// scatters.
+#include "internal.h"
+
+namespace chord {
+namespace {
+
+__device__ __forceinline__ int local_expert(const int32_t* ids, int64_t i, int64_t n, int eb,
+                                            int E) {
+  if (i >= n) return -1;
+  const int g = ids[i] - eb;
+  return (g >= 0 && g < E) ? g : -1;
+}
+
+// Exclusive scan of one int per thread across the workgroup (blockDim.x a
+// multiple of 64, at most 1024).  `tmp` holds >= 16 ints of LDS.  Returns the
+// exclusive prefix; *total receives the sum.
+__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int base = 0, sum = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = tmp[w];
+    if (w < wave) base += t;
+    sum += t;
+  }
+  __syncthreads();
+  *total = sum;
+  return base + x - v;
+}
+
+// One round: every thread takes entry i (ascending with the thread index) and
+// writes it to its stable position running[e] + (earlier entries of e in this
+// round).  `wcnt` is [waves][E] of zeros on entry and on exit.
+__device__ void scatter_round(const int32_t* __restrict__ ids, int64_t i, int64_t n, int eb, int E,
+                              int* running, int* wcnt, int32_t* __restrict__ sorted_ids) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = local_expert(ids, i, n, eb, E);
+  const bool valid = e >= 0;
+  uint64_t mask = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t m = __ballot(bit);
+    mask &= bit ? m : ~m;
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(mask & lt);
+  const int cnt = __popcll(mask);
+  const bool leader = valid && rank == 0;
+  if (leader) wcnt[wave * E + e] = cnt;
+  __syncthreads();
+  if (valid) {
+    int off = running[e];
+    for (int w = 0; w < wave; ++w) off += wcnt[w * E + e];
+    sorted_ids[off + rank] = (int32_t)i;
+  }
+  __syncthreads();
+  if (leader) {
+    atomicAdd(&running[e], cnt);
+    wcnt[wave * E + e] = 0;
+  }
+  __syncthreads();
+}
+
+// Writes expert_ids for the blocks of expert e and the sentinel into the
+// padding of its group.
+__device__ void write_segment(int e, int seg, int cnt, int padded, int bm, int32_t sentinel,
+                              int32_t* sorted_ids, int32_t* expert_ids) {
+  for (int p = seg + cnt; p < seg + padded; ++p) sorted_ids[p] = sentinel;
+  for (int b = seg / bm; b < (seg + padded) / bm; ++b) expert_ids[b] = e;
+}
+
+__device__ void fill_tail(int64_t ntpp, const AlignArgs& a) {
+  const int32_t sentinel = (int32_t)a.n;
+  for (int64_t p = ntpp + threadIdx.x; p < a.max_padded; p += blockDim.x) a.sorted_ids[p] = sentinel;
+  const int64_t nb = (a.max_padded + a.block_m - 1) / a.block_m;
+  for (int64_t b = ntpp / a.block_m + threadIdx.x; b < nb; b += blockDim.x) a.expert_ids[b] = -1;
+}
+
+// ---- single workgroup path ------------------------------------------------
+__global__ __launch_bounds__(1024) void align_single(AlignArgs a) {
+  extern __shared__ int lds[];
+  const int E = a.num_experts;
+  int* running = lds;              // [E]
+  int* wcnt = lds + E;             // [16][E]
+  int* tmp = lds + 17 * E;         // [16]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) running[e] = 0;
+  for (int x = threadIdx.x; x < 16 * E; x += blockDim.x) wcnt[x] = 0;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < a.n; i += blockDim.x) {
+    const int e = local_expert(a.topk_ids, i, a.n, a.expert_begin, E);
+    if (e >= 0) atomicAdd(&running[e], 1);
+  }
+  __syncthreads();
+  // E <= 1024 = blockDim: thread e owns expert e.
+  const int e = threadIdx.x;
+  const int cnt = e < E ? running[e] : 0;
+  const int padded = ((cnt + a.block_m - 1) / a.block_m) * a.block_m;
+  int total;
+  const int seg = block_exclusive_scan(padded, tmp, &total);
+  if (e < E) {
+    write_segment(e, seg, cnt, padded, a.block_m, (int32_t)a.n, a.sorted_ids, a.expert_ids);
+    running[e] = seg;
+  }
+  if (threadIdx.x == 0) *a.ntpp = total;
+  fill_tail(total, a);
+  __syncthreads();
+  for (int64_t base = 0; base < a.n; base += blockDim.x)
+    scatter_round(a.topk_ids, base + threadIdx.x, a.n, a.expert_begin, E, running, wcnt,
+                  a.sorted_ids);
+}
+
+// ---- multi-workgroup path -------------------------------------------------
+__global__ __launch_bounds__(256) void align_count(AlignArgs a) {
+  extern __shared__ int lds[];
+  const int E = a.num_experts;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) lds[e] = 0;
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t end = min(a.n, begin + kAlignChunk);
+  for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
+    const int e = local_expert(a.topk_ids, i, a.n, a.expert_begin, E);
+    if (e >= 0) atomicAdd(&lds[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    a.chunk_counts[(int64_t)blockIdx.x * E + e] = lds[e];
+}
+
+__global__ __launch_bounds__(1024) void align_offsets(AlignArgs a) {
+  __shared__ int tmp[16];
+  const int E = a.num_experts;
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    for (int c = 0; c < a.nchunks; ++c) {
+      const int v = a.chunk_counts[(int64_t)c * E + e];
+      a.chunk_counts[(int64_t)c * E + e] = cnt;  // exclusive prefix over chunks
+      cnt += v;
+    }
+  }
+  const int padded = ((cnt + a.block_m - 1) / a.block_m) * a.block_m;
+  int total;
+  const int seg = block_exclusive_scan(padded, tmp, &total);
+  if (e < E) {
+    write_segment(e, seg, cnt, padded, a.block_m, (int32_t)a.n, a.sorted_ids, a.expert_ids);
+    a.seg_start[e] = seg;
+  }
+  if (threadIdx.x == 0) *a.ntpp = total;
+  fill_tail(total, a);
+}
+
+__global__ __launch_bounds__(256) void align_scatter(AlignArgs a) {
+  extern __shared__ int lds[];
+  const int E = a.num_experts;
+  int* running = lds;         // [E]
+  int* wcnt = lds + E;        // [4][E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    running[e] = a.seg_start[e] + a.chunk_counts[(int64_t)blockIdx.x * E + e];
+  for (int x = threadIdx.x; x < 4 * E; x += blockDim.x) wcnt[x] = 0;
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t end = min(a.n, begin + kAlignChunk);
+  for (int64_t base = begin; base < end; base += blockDim.x)
+    scatter_round(a.topk_ids, base + threadIdx.x, end, a.expert_begin, E, running, wcnt,
+                  a.sorted_ids);
+}
+
+}  // namespace
+
+hipError_t launch_align(const AlignArgs& a, hipStream_t stream) {
+  const int E = a.num_experts;
+  if (a.n <= kAlignChunk && E <= 512) {
+    const size_t lds = (size_t)(17 * E + 16) * sizeof(int);
+    hipLaunchKernelGGL(align_single, dim3(1), dim3(1024), lds, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(align_count, dim3(a.nchunks), dim3(256), (size_t)E * sizeof(int), stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(align_offsets, dim3(1), dim3(1024), 0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(align_scatter, dim3(a.nchunks), dim3(256), (size_t)5 * E * sizeof(int), stream,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace chord

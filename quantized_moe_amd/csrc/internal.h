@@ -1,0 +1,153 @@
+// Internal declarations shared by the host runtime and the HIP kernels of
+// libchord.so.  Not part of the public ABI (see include/chord.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "chord.h"
+
+namespace chord {
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (gfx950).
+//
+// A weight [E, N, K] is cut into 16-row tiles and 128-wide K chunks.  Each
+// (expert, tile, chunk) is one 1152-byte block, stored tile-major so that a
+// wavefront streaming one tile along K reads contiguous memory:
+//
+//   bytes [0, 1024):   64 lanes x 16 bytes.  Lane l holds the 32 codes of
+//                      tile row r = l % 16 for K range chunk*128 + (l/16)*32
+//                      + [0, 32), i.e. exactly one scale group, as 4 words.
+//                      Word s covers k = base + 8s .. 8s+7; inside a word the
+//                      code of k = 2v sits at bits 4v..4v+3 and the code of
+//                      k = 2v+1 at bits 16+4v..16+4v+3, so one shift and one
+//                      mask give a pair of codes in the two 16-bit halves.
+//   bytes [1024, 1152): 64 bf16 scales in lane order: lane l's group scale.
+//
+// Gate_up weights interleave gate and up rows inside each tile so the fused
+// SiLU*mul epilogue finds both in one lane: tile t, row r = 4q + w holds
+// feature f = 8t + 2q + (w >> 1); w even = gate row f, w odd = up row I + f.
+// Down weights keep natural order: tile t, row r = feature 16t + r.
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 16;
+constexpr int kChunkK = 128;
+constexpr int kGroup = 32;
+constexpr int kBlockWeightBytes = 1024;
+constexpr int kBlockBytes = 1152;
+
+inline size_t packed_bytes(int E, int N, int K) {
+  return (size_t)E * (size_t)(N / kTileRows) * (size_t)(K / kChunkK) * (size_t)kBlockBytes;
+}
+
+// Tile descriptor produced on the device: {local expert, first internal row,
+// number of internal rows (<= tile tokens), unused}.
+struct TileDesc {
+  int32_t expert;
+  int32_t row_begin;
+  int32_t nrows;
+  int32_t pad;
+};
+
+enum Layout : int { kIndexed = 0, kContiguous = 1, kMasked = 2 };
+
+// Device status words at the start of every layer workspace.
+struct DevStatus {
+  int32_t error;   // nonzero: routing validation failed (bit flags)
+  int32_t ntiles;  // tiles written by the tile builder
+  int32_t pad[62];
+};
+
+// Arguments of the tile builder (one workgroup).
+struct TileBuildArgs {
+  int layout;
+  int num_experts;     // E_l
+  int tile_tokens;     // max rows per tile
+  int max_tiles;       // capacity of `tiles`
+  int validate;
+  // indexed
+  const int32_t* expert_ids;
+  const int32_t* ntpp;
+  int block_m;
+  int64_t max_padded;
+  // contiguous
+  const int32_t* m_indices;
+  int64_t M;
+  // masked
+  const int32_t* masked_m;
+  int max_m;
+  // out
+  TileDesc* tiles;
+  DevStatus* status;
+};
+
+// Arguments of one expert GEMM launch (gate_up or down).
+struct GemmArgs {
+  const uint8_t* wpack;  // packed weight of this GEMM
+  int n_tiles;           // N / 16
+  int n_chunks;          // K / 128
+  int K;                 // row length of the B source (elements)
+  const uint16_t* bsrc;  // B rows: x / a (gate_up) or h (down), bf16 [*, K]
+  int layout;
+  int gate_up;           // 1: SiLU*mul epilogue into h; 0: plain store
+  // indexed
+  const int32_t* sorted_ids;
+  int topk;
+  int64_t n_flat;        // T * k (sentinel and bound)
+  // contiguous
+  const int32_t* m_indices;
+  // tiles
+  const TileDesc* tiles;
+  const DevStatus* status;  // ntiles
+  int tile_tokens;
+  int tiles_per_item;    // 16-row weight tiles per work item
+  int items_per_tile;    // n_tiles / tiles_per_item
+  // output
+  uint16_t* out;         // h [rows, I] (gate_up) or y / out rows [*, H] (down)
+  int out_ld;
+  int64_t out_rows;      // rows of `out` (bound)
+  const float* row_weights;  // grouped down only, may be null
+  int64_t n_rows_internal;   // internal row bound (h rows)
+};
+
+struct CombineArgs {
+  const uint16_t* rows;     // y [*, H] bf16
+  const int32_t* topk_ids;  // indexed: local test via ids; null for contiguous
+  const int32_t* flat_to_row;  // contiguous: slot -> row (or -1)
+  const float* topk_weights;
+  int T, k, H;
+  int expert_begin, num_experts;
+  int64_t n_rows;
+  uint16_t* out;
+};
+
+struct AlignArgs {
+  const int32_t* topk_ids;
+  int64_t n;               // T * k
+  int expert_begin, num_experts, block_m;
+  int64_t max_padded;
+  int32_t* sorted_ids;
+  int32_t* expert_ids;
+  int32_t* ntpp;
+  int32_t* chunk_counts;   // workspace [nchunks, E_l]
+  int32_t* seg_start;      // workspace [E_l]
+  int nchunks;
+};
+
+// Launchers (defined in the .hip files).  All enqueue on `stream` and return
+// hipSuccess or the launch error.
+hipError_t launch_pack(const int32_t* q, const uint16_t* s, int E, int N, int K, int gate_up,
+                       uint8_t* dst, hipStream_t stream);
+hipError_t launch_align(const AlignArgs& a, hipStream_t stream);
+hipError_t launch_build_tiles(const TileBuildArgs& a, hipStream_t stream);
+hipError_t launch_gemm(int kernel, int mt, const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream);
+
+constexpr int kAlignChunk = 8192;       // entries per align workgroup
+constexpr int kMaxExperts = 1024;       // E_l limit (LDS tables)
+constexpr int kMaxSegments = 16384;     // contiguous 128-row chunks limit
+
+}  // namespace chord

@@ -1,0 +1,723 @@
+// Host runtime of libchord.so: argument validation (before any HIP call, so
+// misuse is reported without touching the device), the per-call schedule
+// planner with its memoised plan cache, workspace layout, and the launch
+// sequences of the three layer entry points.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "internal.h"
+
+using namespace chord;
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local std::string g_last_plan;
+
+chord_status fail(chord_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+chord_status hip_fail(hipError_t e, const char* what) {
+  return fail(CHORD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define CHORD_CHECK(expr)                    \
+  do {                                       \
+    chord_status _s = (expr);                \
+    if (_s != CHORD_OK) return _s;           \
+  } while (0)
+
+#define HIP_TRY(expr, what)                       \
+  do {                                            \
+    hipError_t _e = (expr);                       \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+// ---- device check ---------------------------------------------------------
+struct DeviceInfo {
+  bool checked = false;
+  bool ok = false;
+  int cus = 0;
+  char arch[64] = {0};
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+chord_status check_device(int* cus) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(CHORD_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t p;
+    HIP_TRY(hipGetDeviceProperties(&p, dev), "hipGetDeviceProperties");
+    snprintf(d.arch, sizeof(d.arch), "%s", p.gcnArchName);
+    d.ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    d.cus = p.multiProcessorCount;
+    d.checked = true;
+  }
+  if (!d.ok)
+    return fail(CHORD_ERR_UNSUPPORTED, "device %d is %s; only gfx950 (MI355X) is supported", dev,
+                d.arch);
+  if (cus) *cus = d.cus;
+  return CHORD_OK;
+}
+
+// ---- environment overrides (parsed once) ----------------------------------
+struct EnvOverrides {
+  int kernel = 0;
+  int tokens = 0;
+  bool log = false;
+};
+const EnvOverrides& env() {
+  static EnvOverrides e = [] {
+    EnvOverrides o;
+    if (const char* s = getenv("CHORD_W4A16_KERNEL")) o.kernel = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_TOKENS")) o.tokens = atoi(s);
+    if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
+    return o;
+  }();
+  return e;
+}
+
+// ---- planner and plan cache ------------------------------------------------
+struct PlanKey {
+  int mode, T, k, E_g, E_l, H, I, hint, ov_kernel, ov_tokens, cus;
+  int64_t rows;
+  bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(*this)) == 0; }
+};
+struct PlanKeyHash {
+  size_t operator()(const PlanKey& k) const {
+    const unsigned char* p = reinterpret_cast<const unsigned char*>(&k);
+    size_t h = 1469598103934665603ull;
+    for (size_t i = 0; i < sizeof(k); ++i) h = (h ^ p[i]) * 1099511628211ull;
+    return h;
+  }
+};
+struct Plan {
+  int kernel;       // 1 skinny
+  int mt;           // 16-row token tiles per work item
+  int tile_tokens;  // rows per device tile
+  int nt;           // 16-row weight tiles per work item
+  int max_tiles;
+  int grid_gate_up, grid_down;
+  char text[160];
+};
+std::mutex g_plan_mu;
+std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
+
+int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
+  return (int)((rows + tile_tokens - 1) / tile_tokens) + E_l + 1;
+}
+
+// tok_e = expected rows per local expert; the schedule follows it, not the
+// total token count.
+Plan make_plan(const PlanKey& key) {
+  Plan p{};
+  p.kernel = 1;
+  double tok_e;
+  if (key.mode == kIndexed) {
+    const int eg = key.E_g > 0 ? key.E_g : key.E_l;
+    tok_e = (double)key.T * key.k / eg;
+  } else if (key.mode == kMasked) {
+    tok_e = key.hint;
+  } else {
+    tok_e = 128.0;
+  }
+  int mt = (int)((tok_e + 15.0) / 16.0);
+  mt = std::max(1, std::min(4, mt));
+  int kernel = key.ov_kernel ? key.ov_kernel : env().kernel;
+  int tokens = key.ov_tokens ? key.ov_tokens : env().tokens;
+  if (kernel == 1 || kernel == 0) {
+    if (tokens > 0) mt = std::max(1, std::min(4, tokens / 16));
+  }
+  p.kernel = 1;
+  p.mt = mt;
+  p.tile_tokens = mt * 16;
+  p.nt = 2;
+  p.max_tiles = max_tiles_for(key.rows, key.E_l, p.tile_tokens);
+  const int n_tiles_gu = 2 * key.I / 16, n_tiles_dn = key.H / 16;
+  const int64_t items_gu = (int64_t)p.max_tiles * (n_tiles_gu / p.nt);
+  const int64_t items_dn = (int64_t)p.max_tiles * (n_tiles_dn / p.nt);
+  const int64_t target = (int64_t)std::max(key.cus, 1) * 8;
+  p.grid_gate_up = (int)std::max<int64_t>(1, std::min(items_gu, target));
+  p.grid_down = (int)std::max<int64_t>(1, std::min(items_dn, target));
+  snprintf(p.text, sizeof(p.text),
+           "kernel=skinny mt=%d tile_tokens=%d nt=%d wk=4 max_tiles=%d grid_gu=%d grid_dn=%d "
+           "tok_e=%.1f",
+           p.mt, p.tile_tokens, p.nt, p.max_tiles, p.grid_gate_up, p.grid_down, tok_e);
+  return p;
+}
+
+Plan get_plan(const PlanKey& key) {
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) return it->second;
+  Plan p = make_plan(key);
+  g_plans.emplace(key, p);
+  if (env().log) fprintf(stderr, "[chord] plan mode=%d T=%d E_l=%d: %s\n", key.mode, key.T, key.E_l,
+                         p.text);
+  return p;
+}
+
+// ---- kernel-stage profiling (HIP events on the caller's stream) -----------
+struct ProfRecord {
+  hipEvent_t ev[5];
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_pending;
+std::vector<hipEvent_t> g_ev_pool;
+double g_prof_ms[4] = {0, 0, 0, 0};
+int64_t g_prof_calls = 0;
+
+// Records the event for stage boundary `i` (0..4) of the current call.
+struct StageTimer {
+  bool on = false;
+  ProfRecord rec{};
+  hipStream_t stream = nullptr;
+  explicit StageTimer(hipStream_t s) : stream(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+    if (!on) return;
+    for (int i = 0; i < 5; ++i) {
+      if (!g_ev_pool.empty()) {
+        rec.ev[i] = g_ev_pool.back();
+        g_ev_pool.pop_back();
+      } else if (hipEventCreate(&rec.ev[i]) != hipSuccess) {
+        on = false;
+        return;
+      }
+    }
+  }
+  void mark(int i) {
+    if (on) (void)hipEventRecord(rec.ev[i], stream);
+  }
+  void finish() {
+    if (!on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending.push_back(rec);
+    on = false;
+  }
+};
+
+// ---- workspace layout -----------------------------------------------------
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t status, tiles, h, y, total;
+  int max_tiles;
+};
+
+WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
+  WsLayout w{};
+  w.max_tiles = max_tiles_for(rows, E_l, 16);
+  size_t off = 0;
+  w.status = off;
+  off = align_up(off + sizeof(DevStatus), 256);
+  w.tiles = off;
+  off = align_up(off + (size_t)w.max_tiles * sizeof(TileDesc), 256);
+  w.h = off;
+  off = align_up(off + (size_t)rows * I * 2, 256);
+  w.y = off;
+  if (mode == kIndexed) off = align_up(off + (size_t)T * k * H * 2, 256);
+  w.total = off;
+  return w;
+}
+
+// ---- weight handle checks -------------------------------------------------
+chord_status check_weight(const chord_w4a16_weight* w, const char* name, int mode, int role) {
+  if (!w) return fail(CHORD_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (w->magic != CHORD_WEIGHT_MAGIC || w->version != CHORD_WEIGHT_VERSION)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "%s is not a packed chord weight handle", name);
+  if (!w->data) return fail(CHORD_ERR_INVALID_ARGUMENT, "%s has no data", name);
+  if (w->mode != mode)
+    return fail(CHORD_ERR_LAYOUT_MISMATCH, "%s was packed for mode %d, this entry point is mode %d",
+                name, w->mode, mode);
+  if (w->role != role)
+    return fail(CHORD_ERR_LAYOUT_MISMATCH, "%s has role %d, expected %d", name, w->role, role);
+  if (w->group_size != kGroup) return fail(CHORD_ERR_UNSUPPORTED, "%s group size", name);
+  if (w->bytes < packed_bytes(w->num_experts, w->n, w->k))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "%s byte count too small", name);
+  return CHORD_OK;
+}
+
+chord_status check_pair(const chord_w4a16_weight* w13, const chord_w4a16_weight* w2, int mode,
+                        int H, int I) {
+  CHORD_CHECK(check_weight(w13, "w13", mode, CHORD_ROLE_GATE_UP));
+  CHORD_CHECK(check_weight(w2, "w2", mode, CHORD_ROLE_DOWN));
+  if (H <= 0 || I <= 0) return fail(CHORD_ERR_INVALID_ARGUMENT, "H=%d I=%d", H, I);
+  if (w13->n != 2 * I || w13->k != H)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "w13 is [%d,%d], expected [2I=%d, H=%d]", w13->n,
+                w13->k, 2 * I, H);
+  if (w2->n != H || w2->k != I)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "w2 is [%d,%d], expected [H=%d, I=%d]", w2->n, w2->k,
+                H, I);
+  if (w13->num_experts != w2->num_experts)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "w13 has %d experts, w2 %d", w13->num_experts,
+                w2->num_experts);
+  if (w13->num_experts > kMaxExperts)
+    return fail(CHORD_ERR_UNSUPPORTED, "more than %d local experts", kMaxExperts);
+  if ((2 * I / 16) % 2 != 0 || (H / 16) % 2 != 0)
+    return fail(CHORD_ERR_UNSUPPORTED, "H and 2I must be multiples of 32");
+  return CHORD_OK;
+}
+
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+void set_plan_text(const char* mode, const Plan& p) {
+  char b[256];
+  snprintf(b, sizeof(b), "%s: %s", mode, p.text);
+  g_last_plan = b;
+}
+
+// Shared GEMM sequence: tiles -> gate_up -> down.
+chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, uint8_t* wsp,
+                              const chord_w4a16_weight* w13, const chord_w4a16_weight* w2, int H,
+                              int I, const uint16_t* bsrc, int64_t rows_internal,
+                              const int32_t* sorted_ids, int topk, int64_t n_flat,
+                              const int32_t* m_indices, uint16_t* down_out, int64_t down_rows,
+                              const float* row_weights, TileBuildArgs tb, hipStream_t stream,
+                              StageTimer& timer) {
+  DevStatus* status = reinterpret_cast<DevStatus*>(wsp + ws.status);
+  TileDesc* tiles = reinterpret_cast<TileDesc*>(wsp + ws.tiles);
+  uint16_t* h = reinterpret_cast<uint16_t*>(wsp + ws.h);
+  tb.layout = layout;
+  tb.tile_tokens = plan.tile_tokens;
+  tb.max_tiles = std::min(plan.max_tiles, ws.max_tiles);
+  tb.tiles = tiles;
+  tb.status = status;
+  timer.mark(0);
+  HIP_TRY(launch_build_tiles(tb, stream), "tile builder launch");
+  timer.mark(1);
+
+  GemmArgs g{};
+  g.layout = layout;
+  g.sorted_ids = sorted_ids;
+  g.topk = topk;
+  g.n_flat = n_flat;
+  g.m_indices = m_indices;
+  g.tiles = tiles;
+  g.status = status;
+  g.tile_tokens = plan.tile_tokens;
+  g.tiles_per_item = plan.nt;
+  g.n_rows_internal = rows_internal;
+
+  // gate_up: B = activations rows, out = h [rows_internal, I]
+  g.wpack = static_cast<const uint8_t*>(w13->data);
+  g.n_tiles = 2 * I / kTileRows;
+  g.n_chunks = H / kChunkK;
+  g.K = H;
+  g.bsrc = bsrc;
+  g.gate_up = 1;
+  g.items_per_tile = g.n_tiles / plan.nt;
+  g.out = h;
+  g.out_ld = I;
+  g.out_rows = rows_internal;
+  g.row_weights = nullptr;
+  HIP_TRY(launch_gemm(plan.kernel, plan.mt, g, plan.grid_gate_up, stream), "gate_up launch");
+  timer.mark(2);
+
+  // down: B = h, out = y / out rows
+  g.wpack = static_cast<const uint8_t*>(w2->data);
+  g.n_tiles = H / kTileRows;
+  g.n_chunks = I / kChunkK;
+  g.K = I;
+  g.bsrc = h;
+  g.gate_up = 0;
+  g.items_per_tile = g.n_tiles / plan.nt;
+  g.out = down_out;
+  g.out_ld = H;
+  g.out_rows = down_rows;
+  g.row_weights = row_weights;
+  HIP_TRY(launch_gemm(plan.kernel, plan.mt, g, plan.grid_down, stream), "down launch");
+  timer.mark(3);
+  return CHORD_OK;
+}
+
+chord_status finish_validate(uint32_t flags, const WsLayout& ws, uint8_t* wsp, hipStream_t stream) {
+  if (!(flags & CHORD_FLAG_VALIDATE)) return CHORD_OK;
+  int32_t err = 0;
+  HIP_TRY(hipMemcpyAsync(&err, wsp + ws.status, sizeof(err), hipMemcpyDeviceToHost, stream),
+          "status readback");
+  HIP_TRY(hipStreamSynchronize(stream), "stream sync");
+  if (err != 0) return fail(CHORD_ERR_ROUTING, "routing validation failed (flags 0x%x)", err);
+  return CHORD_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// Public C ABI
+// ===========================================================================
+extern "C" {
+
+const char* chord_status_string(chord_status s) {
+  switch (s) {
+    case CHORD_OK: return "CHORD_OK";
+    case CHORD_ERR_INVALID_ARGUMENT: return "CHORD_ERR_INVALID_ARGUMENT";
+    case CHORD_ERR_UNSUPPORTED: return "CHORD_ERR_UNSUPPORTED";
+    case CHORD_ERR_LAYOUT_MISMATCH: return "CHORD_ERR_LAYOUT_MISMATCH";
+    case CHORD_ERR_WORKSPACE: return "CHORD_ERR_WORKSPACE";
+    case CHORD_ERR_ROUTING: return "CHORD_ERR_ROUTING";
+    case CHORD_ERR_HIP: return "CHORD_ERR_HIP";
+  }
+  return "CHORD_ERR_UNKNOWN";
+}
+
+const char* chord_last_error(void) { return g_last_error.c_str(); }
+
+chord_status chord_last_plan(char* buf, size_t n) {
+  if (!buf || n == 0) return CHORD_ERR_INVALID_ARGUMENT;
+  snprintf(buf, n, "%s", g_last_plan.c_str());
+  return CHORD_OK;
+}
+
+const char* chord_version(void) { return "chord-mi355x 0.1 (gfx950)"; }
+
+chord_status chord_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return CHORD_OK;
+}
+
+chord_status chord_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_pending)
+    for (auto e : r.ev) g_ev_pool.push_back(e);
+  g_prof_pending.clear();
+  for (double& m : g_prof_ms) m = 0;
+  g_prof_calls = 0;
+  return CHORD_OK;
+}
+
+chord_status chord_profile_read(double* stage_ms, int64_t* calls) {
+  g_last_error.clear();
+  if (!stage_ms || !calls) return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    HIP_TRY(hipEventSynchronize(r.ev[4]), "hipEventSynchronize");
+    for (int i = 0; i < 4; ++i) {
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, r.ev[i], r.ev[i + 1]), "hipEventElapsedTime");
+      g_prof_ms[i] += ms;
+    }
+    ++g_prof_calls;
+    for (auto e : r.ev) g_ev_pool.push_back(e);
+  }
+  g_prof_pending.clear();
+  for (int i = 0; i < 4; ++i) stage_ms[i] = g_prof_ms[i];
+  *calls = g_prof_calls;
+  return CHORD_OK;
+}
+
+size_t chord_w4a16_packed_bytes(int mode, int role, int E, int N, int K) {
+  if (mode < 0 || mode > 2 || role < 0 || role > 1) return 0;
+  if (E < 1 || N <= 0 || K <= 0 || K % kChunkK != 0 || N % kTileRows != 0) return 0;
+  if (role == CHORD_ROLE_GATE_UP && ((N / 2) % 8 != 0 || N % 2 != 0)) return 0;
+  return packed_bytes(E, N, K);
+}
+
+chord_status chord_w4a16_pack(int mode, int role, const int32_t* qweight, const chord_bf16* scales,
+                              int E, int N, int K, int group_size, void* dst, size_t dst_bytes,
+                              chord_w4a16_weight* handle, void* stream) {
+  g_last_error.clear();
+  if (mode < 0 || mode > 2) return fail(CHORD_ERR_INVALID_ARGUMENT, "mode %d", mode);
+  if (role < 0 || role > 1) return fail(CHORD_ERR_INVALID_ARGUMENT, "role %d", role);
+  if (!qweight || !scales || !dst || !handle)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (group_size != kGroup)
+    return fail(CHORD_ERR_UNSUPPORTED, "group size %d (only 32 is supported)", group_size);
+  if (E < 1 || N <= 0 || K <= 0) return fail(CHORD_ERR_INVALID_ARGUMENT, "E=%d N=%d K=%d", E, N, K);
+  if (K % kChunkK != 0) return fail(CHORD_ERR_UNSUPPORTED, "K=%d must be a multiple of 128", K);
+  if (N % kTileRows != 0) return fail(CHORD_ERR_UNSUPPORTED, "N=%d must be a multiple of 16", N);
+  if (role == CHORD_ROLE_GATE_UP && (N / 2) % 8 != 0)
+    return fail(CHORD_ERR_UNSUPPORTED, "gate_up N=%d: I must be a multiple of 8", N);
+  const size_t need = packed_bytes(E, N, K);
+  if (dst_bytes < need)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "dst has %zu bytes, %zu needed", dst_bytes, need);
+  CHORD_CHECK(check_device(nullptr));
+  HIP_TRY(launch_pack(qweight, scales, E, N, K, role == CHORD_ROLE_GATE_UP ? 1 : 0,
+                      static_cast<uint8_t*>(dst), static_cast<hipStream_t>(stream)),
+          "pack launch");
+  handle->magic = CHORD_WEIGHT_MAGIC;
+  handle->version = CHORD_WEIGHT_VERSION;
+  handle->mode = mode;
+  handle->role = role;
+  handle->num_experts = E;
+  handle->n = N;
+  handle->k = K;
+  handle->group_size = kGroup;
+  handle->data = dst;
+  handle->bytes = need;
+  return CHORD_OK;
+}
+
+int64_t chord_moe_align_max_padded(int T, int k, int num_local_experts, int block_m) {
+  if (T < 0 || k < 1 || num_local_experts < 1 || block_m < 1) return 0;
+  return (int64_t)T * k + (int64_t)num_local_experts * (block_m - 1);
+}
+
+size_t chord_moe_align_workspace_bytes(int T, int k, int num_local_experts, int block_m) {
+  (void)block_m;
+  if (T < 0 || k < 1 || num_local_experts < 1) return 0;
+  const int64_t n = (int64_t)T * k;
+  const int64_t nchunks = (n + kAlignChunk - 1) / kAlignChunk;
+  return (size_t)(nchunks + 1) * num_local_experts * sizeof(int32_t) + 256;
+}
+
+chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_begin,
+                             int num_local_experts, int block_m, int32_t* sorted_ids,
+                             int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                             int64_t max_padded, void* workspace, size_t ws_bytes, uint32_t flags,
+                             void* stream) {
+  g_last_error.clear();
+  (void)flags;
+  if (T < 0 || k < 1) return fail(CHORD_ERR_INVALID_ARGUMENT, "T=%d k=%d", T, k);
+  if (num_local_experts < 1 || num_local_experts > kMaxExperts)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "num_local_experts=%d (1..%d)", num_local_experts,
+                kMaxExperts);
+  if (!valid_bm(block_m))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "block_m=%d (16, 32, 64 or 128)", block_m);
+  if ((T > 0 && !topk_ids) || !sorted_ids || !expert_ids || !num_tokens_post_padded)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const int64_t n = (int64_t)T * k;
+  if (n >= (int64_t)1 << 30) return fail(CHORD_ERR_UNSUPPORTED, "T*k too large");
+  if (max_padded < chord_moe_align_max_padded(T, k, num_local_experts, block_m))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "max_padded=%lld below T*k + E_l*(block_m-1)=%lld",
+                (long long)max_padded,
+                (long long)chord_moe_align_max_padded(T, k, num_local_experts, block_m));
+  const size_t need = chord_moe_align_workspace_bytes(T, k, num_local_experts, block_m);
+  const bool single = n <= kAlignChunk && num_local_experts <= 512;
+  if (!single && (!workspace || ws_bytes < need))
+    return fail(CHORD_ERR_WORKSPACE, "align workspace %zu bytes, %zu needed", ws_bytes, need);
+  CHORD_CHECK(check_device(nullptr));
+  AlignArgs a{};
+  a.topk_ids = topk_ids;
+  a.n = n;
+  a.expert_begin = expert_begin;
+  a.num_experts = num_local_experts;
+  a.block_m = block_m;
+  a.max_padded = max_padded;
+  a.sorted_ids = sorted_ids;
+  a.expert_ids = expert_ids;
+  a.ntpp = num_tokens_post_padded;
+  a.nchunks = (int)((n + kAlignChunk - 1) / kAlignChunk);
+  if (a.nchunks == 0) a.nchunks = 1;
+  if (!single) {
+    a.seg_start = static_cast<int32_t*>(workspace);
+    a.chunk_counts = a.seg_start + num_local_experts;
+  }
+  const hipError_t e = launch_align(a, static_cast<hipStream_t>(stream));
+  HIP_TRY(e, "align launch");
+  g_last_plan = single ? "align: single workgroup" : "align: count/offsets/scatter";
+  return CHORD_OK;
+}
+
+int chord_w4a16_moe_indexed_block_m(int T, int k, int E_g, int E_l, int H, int I) {
+  (void)T; (void)k; (void)E_g; (void)E_l; (void)H; (void)I;
+  return 16;
+}
+
+size_t chord_w4a16_moe_workspace_bytes(int mode, int T, int k, int E_l, int H, int I,
+                                       int64_t rows) {
+  if (mode < 0 || mode > 2 || T < 0 || k < 0 || E_l < 1 || H <= 0 || I <= 0 || rows < 0) return 0;
+  return layer_ws(mode, T, k, E_l, H, I, rows).total;
+}
+
+chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
+                                     const chord_w4a16_weight* w13, const chord_w4a16_weight* w2,
+                                     const int32_t* topk_ids, const float* topk_weights, int k,
+                                     int expert_begin, int num_global_experts,
+                                     const int32_t* sorted_ids, const int32_t* expert_ids,
+                                     const int32_t* num_tokens_post_padded, int64_t max_padded,
+                                     int block_m, chord_bf16* out, void* workspace,
+                                     size_t ws_bytes, const chord_schedule* override,
+                                     uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (T < 0 || k < 1) return fail(CHORD_ERR_INVALID_ARGUMENT, "T=%d k=%d", T, k);
+  CHORD_CHECK(check_pair(w13, w2, CHORD_MODE_INDEXED, H, I));
+  const int E_l = w13->num_experts;
+  if (T == 0) return CHORD_OK;
+  if (!x || !topk_ids || !topk_weights || !sorted_ids || !expert_ids || !num_tokens_post_padded ||
+      !out)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (!valid_bm(block_m))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "block_m=%d (16, 32, 64 or 128)", block_m);
+  if (max_padded < chord_moe_align_max_padded(T, k, E_l, block_m))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "max_padded=%lld below T*k + E_l*(block_m-1)",
+                (long long)max_padded);
+  if ((int64_t)T * k >= ((int64_t)1 << 30) || max_padded >= ((int64_t)1 << 31))
+    return fail(CHORD_ERR_UNSUPPORTED, "routing tensors too large");
+  if (override && (override->kernel < 0 || override->kernel > 1 || override->tokens < 0 ||
+                   override->tokens % 16 != 0 || override->tokens > 64))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
+  const WsLayout ws = layer_ws(kIndexed, T, k, E_l, H, I, max_padded);
+  if (!workspace || ws_bytes < ws.total)
+    return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
+  int cus = 0;
+  CHORD_CHECK(check_device(&cus));
+  const PlanKey key{kIndexed, T, k, num_global_experts, E_l, H, I, block_m,
+                    override ? override->kernel : 0, override ? override->tokens : 0, cus,
+                    max_padded};
+  const Plan plan = get_plan(key);
+  set_plan_text("indexed", plan);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  TileBuildArgs tb{};
+  tb.num_experts = E_l;
+  tb.validate = (flags & CHORD_FLAG_VALIDATE) ? 1 : 0;
+  tb.expert_ids = expert_ids;
+  tb.ntpp = num_tokens_post_padded;
+  tb.block_m = block_m;
+  tb.max_padded = max_padded;
+  uint16_t* y = reinterpret_cast<uint16_t*>(wsp + ws.y);
+  StageTimer timer(st);
+  CHORD_CHECK(run_expert_gemms(kIndexed, plan, ws, wsp, w13, w2, H, I, x, max_padded, sorted_ids,
+                               k, (int64_t)T * k, nullptr, y, (int64_t)T * k, nullptr, tb, st,
+                               timer));
+  CombineArgs c{};
+  c.rows = y;
+  c.topk_ids = topk_ids;
+  c.flat_to_row = nullptr;
+  c.topk_weights = topk_weights;
+  c.T = T;
+  c.k = k;
+  c.H = H;
+  c.expert_begin = expert_begin;
+  c.num_experts = E_l;
+  c.n_rows = (int64_t)T * k;
+  c.out = out;
+  HIP_TRY(launch_combine(c, st), "combine launch");
+  timer.mark(4);
+  timer.finish();
+  return finish_validate(flags, ws, wsp, st);
+}
+
+chord_status chord_w4a16_moe_grouped_contiguous(
+    const chord_bf16* a, int64_t M, const int32_t* m_indices, int64_t valid_m_hint,
+    const chord_w4a16_weight* w13, const chord_w4a16_weight* w2, int H, int I,
+    const float* row_weights, const int32_t* flat_to_row, int T, int k, const float* topk_weights,
+    chord_bf16* out_rows, chord_bf16* out_tokens, void* workspace, size_t ws_bytes,
+    const chord_schedule* override, uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (override)
+    return fail(CHORD_ERR_INVALID_ARGUMENT,
+                "grouped dispatch chooses its own schedule; overrides are rejected");
+  CHORD_CHECK(check_pair(w13, w2, CHORD_MODE_CONTIGUOUS, H, I));
+  const int E_l = w13->num_experts;
+  if (M < 0 || M % 128 != 0) return fail(CHORD_ERR_INVALID_ARGUMENT, "M=%lld must be a multiple of 128", (long long)M);
+  if (M / 128 > kMaxSegments) return fail(CHORD_ERR_UNSUPPORTED, "M too large");
+  const bool want_tokens = out_tokens != nullptr;
+  if (want_tokens && (!flat_to_row || !topk_weights || T < 0 || k < 1))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "token combine needs flat_to_row, topk_weights, T, k");
+  if (M == 0) {
+    if (want_tokens && T > 0) {
+      CHORD_CHECK(check_device(nullptr));
+      HIP_TRY(launch_zero(out_tokens, (int64_t)T * H, static_cast<hipStream_t>(stream)), "zero");
+    }
+    return CHORD_OK;
+  }
+  if (!a || !m_indices || !out_rows) return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const WsLayout ws = layer_ws(kContiguous, T, k, E_l, H, I, M);
+  if (!workspace || ws_bytes < ws.total)
+    return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
+  int cus = 0;
+  CHORD_CHECK(check_device(&cus));
+  const PlanKey key{kContiguous, T, k, 0, E_l, H, I, (int)std::min<int64_t>(valid_m_hint, 1 << 30),
+                    0, 0, cus, M};
+  const Plan plan = get_plan(key);
+  set_plan_text("contiguous", plan);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  TileBuildArgs tb{};
+  tb.num_experts = E_l;
+  tb.validate = (flags & CHORD_FLAG_VALIDATE) ? 1 : 0;
+  tb.m_indices = m_indices;
+  tb.M = M;
+  StageTimer timer(st);
+  CHORD_CHECK(run_expert_gemms(kContiguous, plan, ws, wsp, w13, w2, H, I, a, M, nullptr, 1, 0,
+                               m_indices, out_rows, M, row_weights, tb, st, timer));
+  if (want_tokens && T > 0) {
+    CombineArgs c{};
+    c.rows = out_rows;
+    c.topk_ids = nullptr;
+    c.flat_to_row = flat_to_row;
+    c.topk_weights = topk_weights;
+    c.T = T;
+    c.k = k;
+    c.H = H;
+    c.num_experts = E_l;
+    c.n_rows = M;
+    c.out = out_tokens;
+    HIP_TRY(launch_combine(c, st), "combine launch");
+  }
+  timer.mark(4);
+  timer.finish();
+  return finish_validate(flags, ws, wsp, st);
+}
+
+chord_status chord_w4a16_moe_grouped_masked(const chord_bf16* a, int E, int max_m,
+                                            const int32_t* masked_m, int expected_m,
+                                            const chord_w4a16_weight* w13,
+                                            const chord_w4a16_weight* w2, int H, int I,
+                                            const float* row_weights, chord_bf16* out,
+                                            void* workspace, size_t ws_bytes,
+                                            const chord_schedule* override, uint32_t flags,
+                                            void* stream) {
+  g_last_error.clear();
+  if (override)
+    return fail(CHORD_ERR_INVALID_ARGUMENT,
+                "grouped dispatch chooses its own schedule; overrides are rejected");
+  if (expected_m <= 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "expected_m=%d must be positive", expected_m);
+  CHORD_CHECK(check_pair(w13, w2, CHORD_MODE_MASKED, H, I));
+  if (E != w13->num_experts)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "E=%d but the weights hold %d experts", E,
+                w13->num_experts);
+  if (max_m < 0) return fail(CHORD_ERR_INVALID_ARGUMENT, "max_m=%d", max_m);
+  if (max_m == 0) return CHORD_OK;
+  if (!a || !masked_m || !out) return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  const int64_t rows = (int64_t)E * max_m;
+  if (rows >= ((int64_t)1 << 31)) return fail(CHORD_ERR_UNSUPPORTED, "E*max_m too large");
+  const WsLayout ws = layer_ws(kMasked, 0, 0, E, H, I, rows);
+  if (!workspace || ws_bytes < ws.total)
+    return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
+  int cus = 0;
+  CHORD_CHECK(check_device(&cus));
+  const PlanKey key{kMasked, 0, 0, 0, E, H, I, expected_m, 0, 0, cus, rows};
+  const Plan plan = get_plan(key);
+  set_plan_text("masked", plan);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  TileBuildArgs tb{};
+  tb.num_experts = E;
+  tb.validate = (flags & CHORD_FLAG_VALIDATE) ? 1 : 0;
+  tb.masked_m = masked_m;
+  tb.max_m = max_m;
+  StageTimer timer(st);
+  CHORD_CHECK(run_expert_gemms(kMasked, plan, ws, wsp, w13, w2, H, I, a, rows, nullptr, 1, 0,
+                               nullptr, out, rows, row_weights, tb, st, timer));
+  timer.mark(4);
+  timer.finish();
+  return finish_validate(flags, ws, wsp, st);
+}
+
+}  // extern "C"

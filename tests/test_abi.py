@@ -1,0 +1,139 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and rejects misuse on the host before any HIP call (no GPU needed:
+every call here fails validation first)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_amd import chord as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "chord.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(chord_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(C.lib, n), n
+    assert sorted(C.EXPORTED) == names
+
+
+def test_status_strings_and_version():
+    assert C.lib.chord_status_string(0) == b"CHORD_OK"
+    assert C.lib.chord_status_string(3) == b"CHORD_ERR_LAYOUT_MISMATCH"
+    assert b"gfx950" in C.lib.chord_version()
+
+
+def test_packed_bytes_and_bounds():
+    assert C.chord_w4a16_packed_bytes(0, 0, 48, 4096, 7168) == 48 * 4096 * 7168 * 9 // 16
+    assert C.chord_w4a16_packed_bytes(0, 1, 1, 16, 100) == 0        # K % 128
+    assert C.chord_w4a16_packed_bytes(0, 0, 1, 24, 128) == 0        # I % 8 for gate_up
+    assert C.chord_moe_align_max_padded(64, 8, 48, 16) == 512 + 48 * 15
+    assert C.chord_w4a16_moe_indexed_block_m(64, 8, 384, 48, 7168, 2048) in (16, 32, 64, 128)
+
+
+def _handle(mode, role, E=2, N=256, K=256):
+    h = C.Weight()
+    h.magic, h.version, h.mode, h.role = 0x43573441, 1, mode, role
+    h.num_experts, h.n, h.k, h.group_size = E, N, K, 32
+    h.data, h.bytes = 0x2000, E * N * K * 9 // 16
+    return h
+
+
+def _indexed(h13, h2, T=4, H=256, I=128, k=2, bm=16, max_padded=None, ws=1 << 30, ov=None, null_x=False):
+    mp = max_padded if max_padded is not None else T * k + 2 * (bm - 1)
+    return C.lib.chord_w4a16_moe_indexed(
+        None if null_x else FAKE, T, H, I, ctypes.byref(h13), ctypes.byref(h2), FAKE, FAKE, k, 0, 8,
+        FAKE, FAKE, FAKE, mp, bm, FAKE, FAKE, ws, ov, 0, None)
+
+
+def test_pack_rejects_unsupported_schemes_on_host():
+    h = C.Weight()
+    assert C.lib.chord_w4a16_pack(0, 0, FAKE, FAKE, 1, 256, 256, 64, FAKE, 1 << 20, ctypes.byref(h), None) == 2
+    assert C.lib.chord_w4a16_pack(0, 0, FAKE, FAKE, 1, 256, 200, 32, FAKE, 1 << 20, ctypes.byref(h), None) == 2
+    assert C.lib.chord_w4a16_pack(0, 1, None, FAKE, 1, 256, 256, 32, FAKE, 1 << 20, ctypes.byref(h), None) == 1
+    assert C.lib.chord_w4a16_pack(0, 1, FAKE, FAKE, 1, 256, 256, 32, FAKE, 10, ctypes.byref(h), None) == 1
+    assert C.lib.chord_w4a16_pack(7, 1, FAKE, FAKE, 1, 256, 256, 32, FAKE, 1 << 20, ctypes.byref(h), None) == 1
+    assert C.lib.chord_w4a16_pack(0, 0, FAKE, FAKE, 1, 256, 256, 16, FAKE, 1 << 20,
+                                  ctypes.byref(h), None) == 2
+    assert b"group size" in C.lib.chord_last_error()
+
+
+def test_layer_rejects_wrong_mode_and_role():
+    assert _indexed(_handle(1, 0), _handle(0, 1, N=256, K=128)) == 3      # contiguous weight, indexed call
+    assert b"mode" in C.lib.chord_last_error()
+    assert _indexed(_handle(0, 1), _handle(0, 1, N=256, K=128)) == 3      # role mismatch
+
+
+def test_layer_host_validation():
+    h13, h2 = _handle(0, 0), _handle(0, 1, N=256, K=128)
+    assert _indexed(h13, h2, null_x=True) == 1
+    assert _indexed(h13, h2, bm=24) == 1
+    assert _indexed(h13, h2, max_padded=3) == 1
+    assert _indexed(h13, h2, ws=16) == 4
+    assert _indexed(h13, h2, I=64) == 1                                   # shape mismatch with handle
+    bad = C.Schedule()
+    bad.kernel = 9
+    assert _indexed(h13, h2, ov=ctypes.byref(bad)) == 1
+    # T == 0 is a no-op that never touches the device
+    assert _indexed(h13, h2, T=0) == 0
+
+
+def test_grouped_rejects_overrides_and_bad_expected_m():
+    s = C.Schedule()
+    hc13, hc2 = _handle(1, 0), _handle(1, 1, N=256, K=128)
+    assert C.lib.chord_w4a16_moe_grouped_contiguous(
+        FAKE, 128, FAKE, 0, ctypes.byref(hc13), ctypes.byref(hc2), 256, 128, None, None, 0, 1, None,
+        FAKE, None, FAKE, 1 << 30, ctypes.byref(s), 0, None) == 1
+    assert b"override" in C.lib.chord_last_error()
+    assert C.lib.chord_w4a16_moe_grouped_contiguous(
+        FAKE, 100, FAKE, 0, ctypes.byref(hc13), ctypes.byref(hc2), 256, 128, None, None, 0, 1, None,
+        FAKE, None, FAKE, 1 << 30, None, 0, None) == 1                    # M % 128
+    hm13, hm2 = _handle(2, 0), _handle(2, 1, N=256, K=128)
+    assert C.lib.chord_w4a16_moe_grouped_masked(
+        FAKE, 2, 16, FAKE, 0, ctypes.byref(hm13), ctypes.byref(hm2), 256, 128, None, FAKE, FAKE,
+        1 << 30, None, 0, None) == 1                                      # expected_m <= 0
+    assert C.lib.chord_w4a16_moe_grouped_masked(
+        FAKE, 2, 16, FAKE, 4, ctypes.byref(hc13), ctypes.byref(hc2), 256, 128, None, FAKE, FAKE,
+        1 << 30, None, 0, None) == 3                                      # prefill weight in decode
+    assert C.lib.chord_w4a16_moe_grouped_masked(
+        FAKE, 3, 16, FAKE, 4, ctypes.byref(hm13), ctypes.byref(hm2), 256, 128, None, FAKE, FAKE,
+        1 << 30, None, 0, None) == 1                                      # E mismatch
+    assert C.lib.chord_w4a16_moe_grouped_masked(
+        FAKE, 2, 16, FAKE, 4, ctypes.byref(hm13), ctypes.byref(hm2), 256, 128, None, FAKE, FAKE,
+        64, None, 0, None) == 4                                           # workspace
+
+
+def test_align_host_validation():
+    assert C.lib.chord_moe_align(FAKE, 4, 2, 0, 8, 16, FAKE, FAKE, FAKE, 3, FAKE, 1 << 20, 0, None) == 1
+    assert C.lib.chord_moe_align(FAKE, 4, 2, 0, 8, 12, FAKE, FAKE, FAKE, 1000, FAKE, 1 << 20, 0, None) == 1
+    assert C.lib.chord_moe_align(FAKE, 4, 2, 0, 0, 16, FAKE, FAKE, FAKE, 1000, FAKE, 1 << 20, 0, None) == 1
+    # large inputs need a workspace
+    assert C.lib.chord_moe_align(FAKE, 8192, 8, 0, 48, 16, FAKE, FAKE, FAKE, 70000, None, 0, 0, None) == 4
+
+
+def test_workspace_query_grows_with_rows():
+    a = C.chord_w4a16_moe_workspace_bytes(0, 64, 8, 48, 7168, 2048, 1232)
+    b = C.chord_w4a16_moe_workspace_bytes(0, 64, 8, 48, 7168, 2048, 5000)
+    assert 0 < a < b
+    assert C.chord_w4a16_moe_workspace_bytes(0, 64, 8, 0, 7168, 2048, 1232) == 0
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "quantized_moe_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", txt, re.M), f
+                assert "oracle/" not in txt, f

@@ -1,0 +1,362 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Alignment tensors must match bit for bit; the bf16 layer output must match
+within |gpu - ref| <= 2e-2 * rms(ref) + 1e-2 * |ref| (tests/tolerance.py).
+Full-size workloads are checked on sampled tokens / rows the oracle can
+compute one by one, in the same launch configuration the benchmark uses.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import gen as G
+from moe_inputs.configs import TINY, DECODE, PREFILL, tp_slice, masked_zipf
+from tests.gpu_util import banner, dev, dev_bf16, host, host_bf16
+from tests.tolerance import check_close
+
+pytestmark = pytest.mark.gpu
+
+C = None
+
+
+def setup_module(module):
+    global C
+    from quantized_moe_amd import chord
+    C = chord
+    banner(f"library {C.version()} on {torch.cuda.get_device_name(0)}")
+
+
+def small_case(seed, T, H, I, E_g, E_l, k, expert_begin=0, logits="normal"):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = G.draw_activations(rng, T, H)
+    ids, w = G.draw_routing(rng, T, E_g, k, logits)
+    q13, s13 = G.draw_weights(rng, E_l, 2 * I, H, scale_mult=(256.0 / H) ** 0.5)
+    q2, s2 = G.draw_weights(rng, E_l, H, I, scale_mult=(256.0 / I) ** 0.5)
+    return x, ids, w, q13, s13, q2, s2, expert_begin
+
+
+def run_indexed(x, ids, w, q13, s13, q2, s2, eb, E_g, bm=16, extra=0, override=None, flags=0,
+                layer=None):
+    from quantized_moe_amd.moe import W4A16MoE
+    if layer is None:
+        layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2))
+    T, k = ids.shape
+    ids_d = dev(ids)
+    mp = C.chord_moe_align_max_padded(T, k, q13.shape[0], bm) + extra
+    al = C.chord_moe_align(ids_d, eb, q13.shape[0], bm, max_padded=mp)
+    out = layer.indexed(dev_bf16(x), ids_d, dev(w), expert_begin=eb, num_global_experts=E_g,
+                        align=(*al, bm), override=override, flags=flags)
+    torch.cuda.synchronize()
+    return host_bf16(out), layer, al
+
+
+# ---------------------------------------------------------------------------
+# alignment: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,E_g,E_l,eb,bm,extra", [
+    (16, 2, 8, 8, 0, 16, 0),            # tiny layer
+    (64, 8, 384, 48, 0, 16, 0),         # decode EP share
+    (64, 8, 384, 48, 96, 32, 1000),     # another rank, oversize buffers
+    (8192, 8, 384, 48, 0, 16, 0),       # prefill: multi-workgroup path
+    (1, 8, 384, 384, 0, 16, 0),         # TP slice, one token
+    (4096, 8, 384, 384, 0, 64, 33),     # TP slice, multi-workgroup
+    (300, 4, 1024, 700, 5, 128, 7),     # more than 512 local experts
+    (0, 8, 384, 48, 0, 16, 5),          # no tokens
+])
+def test_align_bit_exact(T, k, E_g, E_l, eb, bm, extra):
+    banner(f"align T={T} k={k} E_g={E_g} E_l={E_l} eb={eb} bm={bm} extra={extra}")
+    rng = np.random.default_rng(T * 7 + bm)
+    ids = G.draw_routing(rng, T, E_g, k)[0] if T else np.zeros((0, k), np.int32)
+    mp = C.chord_moe_align_max_padded(T, k, E_l, bm) + extra
+    s, e, n = C.chord_moe_align(dev(ids) if T else torch.zeros((0, k), dtype=torch.int32, device="cuda"),
+                                eb, E_l, bm, max_padded=mp)
+    torch.cuda.synchronize()
+    rs, re_, rn = oracle.moe_align(ids, eb, E_l, bm, mp)
+    assert int(host(n)[0]) == rn
+    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(e), re_)
+
+
+def test_align_deterministic_repeat():
+    banner("align repeat determinism T=8192")
+    rng = np.random.default_rng(3)
+    ids = dev(G.draw_routing(rng, 8192, 384, 8, "uniform")[0])
+    a = [host(t).copy() for t in C.chord_moe_align(ids, 0, 48, 16)]
+    b = [host(t).copy() for t in C.chord_moe_align(ids, 0, 48, 16)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# indexed layer
+# ---------------------------------------------------------------------------
+
+def test_indexed_tiny_workload_full_output():
+    wl = G.make_workload(TINY)
+    banner(f"indexed {TINY.name}")
+    got, _, _ = run_indexed(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2, 0,
+                            wl.E_g, bm=16)
+    ref = oracle.moe_layer(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2, 0)
+    st = check_close(got, ref, TINY.name)
+    banner(f"  {st}")
+
+
+@pytest.mark.parametrize("T,H,I,E_g,E_l,k,eb", [
+    (37, 256, 128, 16, 6, 4, 3),        # ragged tokens, expert_begin != 0, non-local slots
+    (5, 384, 256, 8, 8, 8, 0),          # k = E: every expert active
+    (129, 512, 384, 32, 32, 2, 0),      # several 16-row tiles, I not a power of two
+    (1, 256, 128, 64, 4, 8, 0),         # single token, likely no local hit
+])
+def test_indexed_small_shapes(T, H, I, E_g, E_l, k, eb):
+    banner(f"indexed small T={T} H={H} I={I} E_g={E_g} E_l={E_l} k={k} eb={eb}")
+    case = small_case(T * 31 + H, T, H, I, E_g, E_l, k, eb)
+    got, _, _ = run_indexed(*case, E_g=E_g, bm=16)
+    ref = oracle.moe_layer(*case)
+    check_close(got, ref)
+
+
+@pytest.mark.parametrize("tokens", [16, 32, 48, 64])
+def test_indexed_schedule_overrides_bit_identical(tokens):
+    """Schedules differ only in tiling of tokens: results must be bit-identical."""
+    banner(f"indexed schedule override tokens={tokens}")
+    case = small_case(99, 70, 256, 128, 8, 8, 4)
+    base, layer, _ = run_indexed(*case, E_g=8, bm=16, override={"kernel": 1, "tokens": 16})
+    got, _, _ = run_indexed(*case, E_g=8, bm=16, override={"kernel": 1, "tokens": tokens},
+                            layer=layer)
+    assert np.array_equal(got, base)
+    check_close(got, oracle.moe_layer(*case))
+
+
+@pytest.mark.parametrize("bm,extra", [(32, 0), (64, 500), (128, 1)])
+def test_indexed_block_m_and_oversize_buffers(bm, extra):
+    banner(f"indexed bm={bm} extra={extra}")
+    case = small_case(5 + bm, 40, 256, 128, 16, 16, 4)
+    got, _, _ = run_indexed(*case, E_g=16, bm=bm, extra=extra)
+    check_close(got, oracle.moe_layer(*case))
+
+
+def test_indexed_no_local_tokens_give_zero():
+    banner("indexed: no local slots")
+    case = small_case(11, 9, 256, 128, 64, 4, 2, expert_begin=60)
+    x, ids, w, *rest = case
+    ids = np.where(ids >= 60, ids - 8, ids).astype(np.int32)  # nothing in [60, 64)
+    got, _, _ = run_indexed(x, ids, w, *rest, E_g=64)
+    assert np.all(got == 0)
+
+
+def test_indexed_repeat_is_bitwise_deterministic():
+    banner("indexed determinism")
+    case = small_case(12, 64, 512, 256, 16, 16, 4)
+    a, layer, _ = run_indexed(*case, E_g=16)
+    b, _, _ = run_indexed(*case, E_g=16, layer=layer)
+    assert np.array_equal(a, b)
+
+
+def test_indexed_validate_flag_passes_good_routing():
+    banner("indexed validate flag")
+    case = small_case(13, 20, 256, 128, 8, 8, 2)
+    got, _, _ = run_indexed(*case, E_g=8, flags=C.FLAG_VALIDATE)
+    check_close(got, oracle.moe_layer(*case))
+
+
+def test_indexed_validate_flag_reports_bad_expert_ids():
+    """A corrupted expert_ids entry is skipped in trusted mode and reported as
+    CHORD_ERR_ROUTING with validation on (forced from the host; the kernels
+    never index out of bounds)."""
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("indexed validate flag with corrupted expert_ids")
+    x, ids, w, q13, s13, q2, s2, eb = small_case(14, 20, 256, 128, 8, 8, 2)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2))
+    ids_d = dev(ids)
+    s, e, n = C.chord_moe_align(ids_d, 0, 8, 16)
+    e[0] = 99
+    with pytest.raises(C.ChordError) as ei:
+        layer.indexed(dev_bf16(x), ids_d, dev(w), 0, 8, align=(s, e, n, 16), flags=C.FLAG_VALIDATE)
+    assert ei.value.status == 5
+    layer.indexed(dev_bf16(x), ids_d, dev(w), 0, 8, align=(s, e, n, 16))  # trusted: no error
+    torch.cuda.synchronize()
+
+
+def _sample_tokens(ids, eb, E_l, n, seed):
+    has = np.nonzero(np.any((ids >= eb) & (ids < eb + E_l), axis=1))[0]
+    none = np.nonzero(~np.any((ids >= eb) & (ids < eb + E_l), axis=1))[0]
+    rng = np.random.default_rng(seed)
+    pick = list(rng.choice(has, size=min(n, has.size), replace=False))
+    if none.size:
+        pick.append(int(none[0]))
+    return sorted(int(t) for t in pick)
+
+
+@pytest.mark.parametrize("spec", [DECODE, tp_slice(1), tp_slice(32), tp_slice(512), tp_slice(4096),
+                                  PREFILL], ids=lambda s: s.name)
+def test_indexed_full_size_sampled(spec):
+    banner(f"indexed full size {spec.name}: drawing inputs")
+    wl = G.make_workload(spec)
+    banner(f"indexed full size {spec.name}: GPU run")
+    got, _, _ = run_indexed(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2,
+                            wl.expert_begin, wl.E_g, bm=C.chord_w4a16_moe_indexed_block_m(
+                                wl.T, wl.k, wl.E_g, wl.E_l, wl.H, wl.I))
+    toks = _sample_tokens(wl.topk_ids, wl.expert_begin, wl.E_l, 3 if wl.T > 1000 else 6, 0)
+    banner(f"indexed full size {spec.name}: oracle on tokens {toks}")
+    ref = oracle.moe_layer(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2,
+                           wl.expert_begin, tokens=toks)
+    st = check_close(got[toks], ref, spec.name)
+    banner(f"  {st}")
+    # tokens with no local slot are exactly zero
+    none = ~np.any((wl.topk_ids >= wl.expert_begin) & (wl.topk_ids < wl.expert_begin + wl.E_l), axis=1)
+    assert np.all(got[none] == 0)
+    assert np.all(np.isfinite(got.view(np.int16).astype(np.float64)))
+
+
+# ---------------------------------------------------------------------------
+# grouped layouts
+# ---------------------------------------------------------------------------
+
+def test_contiguous_small_with_token_combine():
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("contiguous small + combine")
+    x, ids, w, q13, s13, q2, s2, eb = small_case(21, 90, 256, 128, 12, 6, 3)
+    a, m_idx, f2r, nvalid = G.build_contiguous(ids, x, eb, 6)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_CONTIGUOUS)
+    T = ids.shape[0]
+    out_tokens = torch.empty((T, 256), dtype=torch.bfloat16, device="cuda")
+    rows, tok = layer.contiguous(dev_bf16(a), dev(m_idx), nvalid, flat_to_row=dev(f2r),
+                                 topk_weights=dev(w), out_tokens=out_tokens)
+    torch.cuda.synchronize()
+    rows_h = host_bf16(rows)
+    ref_rows = oracle.grouped_contiguous(a, m_idx, q13, s13, q2, s2)
+    valid = m_idx >= 0
+    check_close(rows_h[valid], ref_rows[valid], "contiguous rows")
+    check_close(host_bf16(tok), oracle.moe_layer(x, ids, w, q13, s13, q2, s2, eb), "contiguous tokens")
+
+
+def test_contiguous_row_weights():
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("contiguous row weights")
+    x, ids, w, q13, s13, q2, s2, eb = small_case(22, 30, 256, 128, 4, 4, 2)
+    a, m_idx, f2r, nvalid = G.build_contiguous(ids, x, eb, 4)
+    rw = np.random.default_rng(0).uniform(0.1, 1.0, a.shape[0]).astype(np.float32)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_CONTIGUOUS)
+    rows, _ = layer.contiguous(dev_bf16(a), dev(m_idx), nvalid, row_weights=dev(rw))
+    torch.cuda.synchronize()
+    ref = oracle.grouped_contiguous(a, m_idx, q13, s13, q2, s2, row_weights=rw)
+    valid = m_idx >= 0
+    check_close(host_bf16(rows)[valid], ref[valid])
+
+
+def test_contiguous_prefill_same_draw_sampled():
+    from quantized_moe_amd.moe import W4A16MoE
+    wl = G.make_workload(PREFILL)
+    banner("contiguous prefill: dispatch")
+    a, m_idx, f2r, nvalid = G.build_contiguous(wl.topk_ids, wl.x, 0, wl.E_l)
+    layer = W4A16MoE(dev(wl.q13), dev_bf16(wl.s13), dev(wl.q2), dev_bf16(wl.s2),
+                     mode=C.MODE_CONTIGUOUS)
+    banner(f"contiguous prefill: GPU run M={a.shape[0]}")
+    rows, _ = layer.contiguous(dev_bf16(a), dev(m_idx), nvalid)
+    torch.cuda.synchronize()
+    rows_h = host_bf16(rows)
+    rng = np.random.default_rng(1)
+    valid_rows = np.nonzero(m_idx >= 0)[0]
+    # rows of two experts, including each segment's last row (ragged tail)
+    pick = set(rng.choice(valid_rows, 6, replace=False).tolist())
+    for e in (0, wl.E_l - 1):
+        seg = np.nonzero(m_idx == e)[0]
+        pick |= {int(seg[0]), int(seg[-1])}
+    pick = sorted(pick)
+    banner(f"contiguous prefill: oracle rows {pick}")
+    ref = oracle.grouped_contiguous(a, m_idx, wl.q13, wl.s13, wl.q2, wl.s2, rows=pick)
+    check_close(rows_h[pick], ref, "contiguous prefill rows")
+
+
+def test_masked_small():
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("masked small")
+    rng = np.random.default_rng(31)
+    E, max_m, H, I = 6, 40, 256, 128
+    a3, mm, em, _ = G.draw_masked(rng, E, max_m, H)
+    mm[2] = 0
+    mm[3] = max_m
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H)
+    q2, s2 = G.draw_weights(rng, E, H, I)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_MASKED)
+    out = layer.masked(dev_bf16(a3), dev(mm), em)
+    torch.cuda.synchronize()
+    got = host_bf16(out)
+    ref = oracle.grouped_masked(a3, mm, q13, s13, q2, s2)
+    valid = np.zeros(E * max_m, bool)
+    for e in range(E):
+        valid[e * max_m:e * max_m + mm[e]] = True
+    check_close(got[valid], ref[valid], "masked")
+
+
+def test_masked_expected_m_is_only_a_hint():
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("masked expected_m hint")
+    rng = np.random.default_rng(32)
+    E, max_m, H, I = 4, 64, 256, 128
+    a3, mm, em, _ = G.draw_masked(rng, E, max_m, H)
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H)
+    q2, s2 = G.draw_weights(rng, E, H, I)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_MASKED)
+    outs = []
+    for hint in (1, em, 64):
+        o = layer.masked(dev_bf16(a3), dev(mm), hint)
+        torch.cuda.synchronize()
+        outs.append(host_bf16(o))
+    ref = oracle.grouped_masked(a3, mm, q13, s13, q2, s2)
+    for e in range(E):
+        sl = slice(e * max_m, e * max_m + mm[e])
+        for o in outs:
+            check_close(o[sl], ref[sl])
+
+
+def test_masked_validate_reports_overflowing_counts():
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("masked validate: masked_m > max_m")
+    rng = np.random.default_rng(33)
+    E, max_m, H, I = 3, 16, 256, 128
+    a3, mm, em, _ = G.draw_masked(rng, E, max_m, H)
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H)
+    q2, s2 = G.draw_weights(rng, E, H, I)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_MASKED)
+    bad = mm.copy()
+    bad[1] = max_m + 5
+    with pytest.raises(C.ChordError) as ei:
+        layer.masked(dev_bf16(a3), dev(bad), em, flags=C.FLAG_VALIDATE)
+    assert ei.value.status == 5
+    out = layer.masked(dev_bf16(a3), dev(bad), em)       # trusted: clamped to max_m
+    torch.cuda.synchronize()
+    clamped = np.minimum(bad, max_m)
+    ref = oracle.grouped_masked(a3, clamped, q13, s13, q2, s2)
+    got = host_bf16(out)
+    for e in range(E):
+        sl = slice(e * max_m, e * max_m + clamped[e])
+        check_close(got[sl], ref[sl])
+
+
+@pytest.mark.parametrize("E_l", [48, 96, 24])
+def test_masked_zipf_full_size_sampled(E_l):
+    spec = masked_zipf(E_l)
+    banner(f"masked full size {spec.name}: drawing")
+    wl = G.make_workload(spec)
+    from quantized_moe_amd.moe import W4A16MoE
+    layer = W4A16MoE(dev(wl.q13), dev_bf16(wl.s13), dev(wl.q2), dev_bf16(wl.s2), mode=C.MODE_MASKED)
+    banner(f"masked full size {spec.name}: GPU run")
+    out = layer.masked(dev_bf16(wl.a3), dev(wl.masked_m), wl.expected_m)
+    torch.cuda.synchronize()
+    got = host_bf16(out)
+    # hottest expert (several tiles, ragged tail) and a cold one
+    order = np.argsort(-wl.masked_m)
+    for e in (int(order[0]), int(order[len(order) // 2])):
+        m = int(wl.masked_m[e])
+        if m == 0:
+            continue
+        rows = sorted({0, m - 1, m // 2})
+        banner(f"masked full size: oracle expert {e} rows {rows} of {m}")
+        sub = wl.a3[e:e + 1, rows]
+        ref = oracle.grouped_masked(sub, np.array([len(rows)], np.int32), wl.q13[e:e + 1],
+                                    wl.s13[e:e + 1], wl.q2[e:e + 1], wl.s2[e:e + 1])
+        check_close(got[[e * wl.max_m + r for r in rows]], ref, f"masked e={e}")
