@@ -97,9 +97,14 @@ typedef struct {
  * Grouped entry points reject any override ([Novita] §"Gruppierte SM90-Kernel":
  * the grouped dispatch does not accept indexed block_m / tuning overrides). */
 typedef struct {
-  int32_t kernel;     /* 0 auto, 1 skinny (weight-streaming), 2 tile (LDS-staged tokens) */
-  int32_t tokens;     /* tokens per tile: skinny 16/32/48/64, tile 64..256 step 16; 0 auto */
-  int32_t reserved[6];
+  int32_t kernel;      /* 0 auto, 1 weight-streaming GEMMs */
+  int32_t tokens;      /* rows per token tile: 16 or 32; 0 auto */
+  int32_t gate_up_nt;  /* 16-row weight tiles per wave in the gate_up GEMM: 2 or 4; 0 auto */
+  int32_t gate_up_wk;  /* waves splitting K in the gate_up GEMM: 1, 2 or 4; 0 auto */
+  int32_t down_nt;     /* as above for the down GEMM */
+  int32_t down_wk;
+  int32_t prefetch;    /* K chunks in flight per wave: 2 or 4; 0 auto */
+  int32_t reserved;
 } chord_schedule;
 
 /* ---------------------------------------------------------------------------

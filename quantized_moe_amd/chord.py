@@ -48,7 +48,9 @@ class Weight(ctypes.Structure):
 
 class Schedule(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tokens", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("gate_up_nt", ctypes.c_int32), ("gate_up_wk", ctypes.c_int32),
+                ("down_nt", ctypes.c_int32), ("down_wk", ctypes.c_int32),
+                ("prefetch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def _load():
@@ -203,8 +205,9 @@ def _sched(override):
     if override is None:
         return None
     s = Schedule()
-    s.kernel = override.get("kernel", 0)
-    s.tokens = override.get("tokens", 0)
+    for name, _ in Schedule._fields_:
+        if name != "reserved":
+            setattr(s, name, int(override.get(name, 0)))
     return ctypes.byref(s)
 
 

@@ -1,0 +1,337 @@
+// Weight-streaming expert GEMM for few rows per expert (decode, TP slices,
+// masked tails): the layer is HBM-bound there, so every workgroup streams its
+// packed weight tiles straight from HBM into registers, dequantises them and
+// feeds v_mfma_f32_16x16x32_bf16 with the weights as the A operand (16 weight
+// rows) and up to MT x 16 tokens as B operands.
+//
+// Dequantisation is exact: each weight becomes bf16_rne((q - 8) * s), the
+// subtract-then-scale order with one bf16 rounding that the pages keep in
+// their fused nibble extraction ("vLLM x Novita AI: Chord W4A16 INT4 MoE
+// Kernel fuer Kimi K2.x", section "H200 und Blackwell indexierter Decode"):
+//   * one shift + one mask-or turns two codes into the fp16 halves 1024 + q;
+//   * v_fma_mix_f32 computes (1024 + q) * s - 1032 * s with one rounding,
+//     which is exactly (q - 8) * s (at most 11 significant bits);
+//   * v_cvt_pk_bf16_f32 rounds two of them to bf16, nearest-even.
+#include "device_common.h"
+
+namespace chord {
+namespace {
+
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family
+// chips; out-of-range offsets read as zero.
+constexpr int kRsrcWord3 = 0x00020000;
+// Offset that lies past every buffer resource used here (sizes < 3 GiB).
+constexpr uint32_t kNoRow = 0xC0000000u;
+// Cache policy of the one-touch weight stream: non-temporal.
+constexpr int kStreamAux = 2;
+
+// Per-scale constants of the exact dequantisation.  Codes sitting in bits 0..3
+// of a 16-bit half read as fp16 1024 + q; codes in bits 4..7 read as
+// 1024 + 16q (no shift needed).  Then
+//   (1024 + q) * s - 1032 s  =  (1024 + 16q) * (s / 16) - 72 s  =  (q - 8) s,
+// each exact in one fma (the product has at most 11 significant bits).
+struct DqScale {
+  float s, c, s16, c16;
+};
+__device__ __forceinline__ DqScale dq_scale(uint32_t bits16) {
+  const float s = bf16_to_f32(bits16);
+  return DqScale{s, -1032.0f * s, 0.0625f * s, -72.0f * s};
+}
+
+// Four packed words (32 codes of one row, one scale group) -> 4 x 8 bf16
+// weights bf16_rne((q - 8) * s).  Staged so that no result is consumed by the
+// next instruction: masks, then fmas, then conversions.
+__device__ __forceinline__ void dequant_words(const uint4& wq, const DqScale& k, uint32_t mlo,
+                                              uint32_t mhi, uint32_t magic, bf16x8_t out[4]) {
+  const uint32_t w[4] = {wq.x, wq.y, wq.z, wq.w};
+  uint32_t m[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w8 = w[i] >> 8;
+    m[i][0] = and_or(w[i], mlo, magic);  // k = 0, 1     (1024 + q)
+    m[i][1] = and_or(w[i], mhi, magic);  // k = 2, 3     (1024 + 16q)
+    m[i][2] = and_or(w8, mlo, magic);    // k = 4, 5
+    m[i][3] = and_or(w8, mhi, magic);    // k = 6, 7
+  }
+  float f[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const half2_t h = __builtin_bit_cast(half2_t, m[i][v]);
+      const float sv = (v & 1) ? k.s16 : k.s;
+      const float cv = (v & 1) ? k.c16 : k.c;
+      f[i][2 * v] = __builtin_fmaf((float)h[0], sv, cv);
+      f[i][2 * v + 1] = __builtin_fmaf((float)h[1], sv, cv);
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    out[i] = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pk_bf16(f[i][0], f[i][1]), pk_bf16(f[i][2], f[i][3]),
+                             pk_bf16(f[i][4], f[i][5]), pk_bf16(f[i][6], f[i][7])));
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// Row mapping of one tile row: the B source row and the output row, or -1.
+struct RowMap {
+  int64_t src;
+  int64_t dst;
+};
+
+__device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t R) {
+  RowMap m{-1, -1};
+  if (a.layout == kIndexed) {
+    const int64_t f = a.sorted_ids[R];
+    if (f < 0 || f >= a.n_flat) return m;
+    if (a.gate_up) {
+      m.src = f / a.topk;
+      m.dst = R;
+    } else {
+      m.src = R;
+      m.dst = f;
+    }
+  } else if (a.layout == kContiguous) {
+    if (a.m_indices[R] != expert) return m;
+    m.src = R;
+    m.dst = R;
+  } else {
+    m.src = R;
+    m.dst = R;
+  }
+  return m;
+}
+
+// Number of tiles (device tile list, or one tile per alignment block).
+__device__ __forceinline__ int num_tiles(const GemmArgs& a) {
+  if (a.tiles != nullptr) return a.status->ntiles;
+  int64_t ntpp = *a.ntpp;
+  ntpp = ntpp < 0 ? 0 : (ntpp > a.max_padded ? a.max_padded : ntpp);
+  return (int)(ntpp / a.block_m);
+}
+
+// Tile `ti`; expert -1 means "skip" (an out-of-range expert id).
+__device__ __forceinline__ TileDesc get_tile(const GemmArgs& a, int ti) {
+  if (a.tiles != nullptr) return a.tiles[ti];
+  const int e = a.expert_ids[ti];
+  TileDesc t{e, ti * a.block_m, a.block_m, 0};
+  if (e < 0 || e >= a.num_experts) t.expert = -1;
+  return t;
+}
+
+// A workgroup of WK waves owns NT 16-row weight tiles of one expert and up to
+// MT*16 rows of one token tile; the waves split K and reduce through LDS.
+// Per 128-wide K chunk each lane streams 16 bytes of packed codes and one
+// scale per weight tile (one scale group of one row); token rows come from
+// global memory (L2-resident).  Persistent: workgroups stride over
+// (tile, weight-tile group) items.
+template <int NT, int MT, int WK, int PF>
+__global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
+  extern __shared__ float red[];  // [WK][NT*MT][64][4]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int col = lane & 15;
+  const int n_items = num_tiles(a) * a.items_per_tile;
+  const int c_lo = (a.n_chunks * wave) / WK;
+  const int c_hi = (a.n_chunks * (wave + 1)) / WK;
+  const uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int ti = item / a.items_per_tile;
+    const int ng = item % a.items_per_tile;
+    const TileDesc td = get_tile(a, ti);
+    const int e = td.expert;
+    if (e < 0) continue;  // uniform over the workgroup
+
+    // B operand: this lane supplies token `col` of each token tile, read
+    // through a bounds-checked buffer resource; lanes without a token get an
+    // out-of-range offset and read zeros (no branch around the loads).
+    uint32_t xoff[MT];
+    int64_t dst[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + col;
+      xoff[mt] = kNoRow;
+      dst[mt] = -1;
+      if (m < td.nrows) {
+        const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
+        if (rm.src >= 0) {
+          xoff[mt] = (uint32_t)((rm.src * (int64_t)a.K + q * kGroup) * 2);
+          dst[mt] = rm.dst;
+        }
+      }
+    }
+
+    // Weights: one resource over this expert's packed tiles; the chunk and
+    // tile offsets are scalar.
+    const int64_t expert_bytes = (int64_t)a.n_tiles * a.n_chunks * kBlockBytes;
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+    const uint32_t tile0 = (uint32_t)(ng * NT) * a.n_chunks * kBlockBytes;
+
+    f32x4_t acc[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = zero4;
+
+    uint4 wq[PF][NT];
+    uint32_t sc[PF][NT];
+    uint4 xb[2][MT][4];
+
+    auto load_w = [&](int p, int c) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t blk = tile0 + (uint32_t)(nt * a.n_chunks + c) * kBlockBytes;
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+        wq[p][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+        sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+      }
+    };
+    auto load_x = [&](int p, int c) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4_t v =
+              __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[mt], c * kChunkK * 2 + s * 16, 0);
+          xb[p][mt][s] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+    auto compute = [&](int p, int xp) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x8_t av[4];
+        dequant_words(wq[p][nt], dq_scale(sc[p][nt]), kMaskLo, kMaskHi, kMagic, av);
+        // No liveness branch around the MFMA: a dead token tile multiplies
+        // zeros, which costs less than breaking the instruction stream.
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st], as_bf16x8(xb[xp][mt][st]),
+                                                                  acc[nt][mt], 0, 0, 0);
+      }
+    };
+
+    // PF is even, so chunk c_lo + i uses weight slot i % PF and token slot
+    // i % 2, both compile-time inside the unrolled body.
+    // The steady-state body is straight-line: prefetch indices past the last
+    // chunk are clamped to it (a redundant, in-bounds load), so the compiler
+    // can count outstanding loads exactly instead of waiting for all of them.
+    static_assert(PF % 2 == 0, "even prefetch depth");
+    if (c_lo < c_hi) {
+      const int c_last = c_hi - 1;
+      load_x(0, c_lo);
+#pragma unroll
+      for (int p = 0; p < PF; ++p) load_w(p, min(c_lo + p, c_last));
+      int c = c_lo;
+      for (; c + PF <= c_hi; c += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+          load_x((p + 1) & 1, min(c + p + 1, c_last));
+          compute(p, p & 1);
+          load_w(p, min(c + p + PF, c_last));
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < PF - 1; ++p) {
+        if (c + p < c_hi) {
+          load_x((p + 1) & 1, min(c + p + 1, c_last));
+          compute(p, p & 1);
+        }
+      }
+    }
+
+    // Cross-wave K reduction: wave w finishes the (nt, mt) pairs with
+    // (nt * MT + mt) % WK == w.
+    if (WK > 1) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4_t*>(red + (((size_t)wave * NT * MT + nt * MT + mt) * 64 + lane) *
+                                                4) = acc[nt][mt];
+      __syncthreads();
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if ((nt * MT + mt) % WK != wave) continue;
+          f32x4_t sum = zero4;
+          for (int w = 0; w < WK; ++w)
+            sum += *reinterpret_cast<const f32x4_t*>(
+                red + (((size_t)w * NT * MT + nt * MT + mt) * 64 + lane) * 4);
+          acc[nt][mt] = sum;
+        }
+    }
+
+    // Epilogue: lane holds rows 4q..4q+3 of weight tile nt for token `col`.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int tw = ng * NT + nt;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (WK > 1 && (nt * MT + mt) % WK != wave) continue;
+        if (dst[mt] < 0) continue;
+        const f32x4_t v = acc[nt][mt];
+        if (a.gate_up) {
+          const int f0 = tw * 8 + 2 * q;
+          *reinterpret_cast<uint32_t*>(a.out + dst[mt] * (int64_t)a.out_ld + f0) =
+              pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
+        } else {
+          const int n0 = tw * 16 + 4 * q;
+          const float rw = a.row_weights != nullptr ? a.row_weights[dst[mt]] : 1.0f;
+          *reinterpret_cast<uint2*>(a.out + dst[mt] * (int64_t)a.out_ld + n0) =
+              make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
+        }
+      }
+    }
+    if (WK > 1) __syncthreads();  // LDS reuse by the next item
+  }
+}
+
+template <int NT, int MT, int WK, int PF>
+hipError_t launch_stream_t(const GemmArgs& a, int grid, hipStream_t stream) {
+  const size_t lds = WK > 1 ? (size_t)WK * NT * MT * 64 * 4 * sizeof(float) : 0;
+  static const int per_cu = blocks_per_cu(gemm_stream<NT, MT, WK, PF>, 64 * WK, lds);
+  const int cap = per_cu * (a.num_cus > 0 ? a.num_cus : 256);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((gemm_stream<NT, MT, WK, PF>), dim3(grid), dim3(64 * WK), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArgs& a, int grid,
+                       hipStream_t stream) {
+  (void)kernel;
+  const int key = nt * 1000 + mt * 100 + wk * 10 + pf;
+  switch (key) {
+#define CHORD_STREAM_CASE(NT, MT, WK, PF) \
+  case NT * 1000 + MT * 100 + WK * 10 + PF: return launch_stream_t<NT, MT, WK, PF>(a, grid, stream);
+#define CHORD_STREAM_WK(NT, MT, WK) CHORD_STREAM_CASE(NT, MT, WK, 2) CHORD_STREAM_CASE(NT, MT, WK, 4)
+#define CHORD_STREAM_MT(NT, MT) \
+  CHORD_STREAM_WK(NT, MT, 1) CHORD_STREAM_WK(NT, MT, 2) CHORD_STREAM_WK(NT, MT, 4)
+    CHORD_STREAM_MT(2, 1)
+    CHORD_STREAM_MT(2, 2)
+    CHORD_STREAM_MT(4, 1)
+    CHORD_STREAM_MT(4, 2)
+#undef CHORD_STREAM_MT
+#undef CHORD_STREAM_WK
+#undef CHORD_STREAM_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace chord

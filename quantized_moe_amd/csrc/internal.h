@@ -24,7 +24,9 @@ namespace chord {
 //                      Word s covers k = base + 8s .. 8s+7; inside a word the
 //                      code of k = 2v sits at bits 4v..4v+3 and the code of
 //                      k = 2v+1 at bits 16+4v..16+4v+3, so one shift and one
-//                      mask give a pair of codes in the two 16-bit halves.
+//                      mask-or give a pair of codes in the two 16-bit halves.
+//                      MFMA step s of the chunk takes word s of every lane:
+//                      lane group l/16 supplies k = (l/16)*32 + 8s + [0, 8).
 //   bytes [1024, 1152): 64 bf16 scales in lane order: lane l's group scale.
 //
 // Gate_up weights interleave gate and up rows inside each tile so the fused
@@ -90,6 +92,7 @@ struct GemmArgs {
   int n_chunks;          // K / 128
   int K;                 // row length of the B source (elements)
   const uint16_t* bsrc;  // B rows: x / a (gate_up) or h (down), bf16 [*, K]
+  int64_t bsrc_bytes;    // size of bsrc (bounds of the buffer resource, < 3 GiB)
   int layout;
   int gate_up;           // 1: SiLU*mul epilogue into h; 0: plain store
   // indexed
@@ -98,9 +101,16 @@ struct GemmArgs {
   int64_t n_flat;        // T * k (sentinel and bound)
   // contiguous
   const int32_t* m_indices;
-  // tiles
+  // tiles: a device tile list, or (tiles == nullptr, indexed only) one tile
+  // per alignment block of block_m rows read from expert_ids / ntpp.
   const TileDesc* tiles;
   const DevStatus* status;  // ntiles
+  const int32_t* expert_ids;
+  const int32_t* ntpp;
+  int block_m;
+  int64_t max_padded;
+  int num_experts;
+  int num_cus;           // compute units (persistent grid clamp)
   int tile_tokens;
   int tiles_per_item;    // 16-row weight tiles per work item
   int items_per_tile;    // n_tiles / tiles_per_item
@@ -142,7 +152,13 @@ hipError_t launch_pack(const int32_t* q, const uint16_t* s, int E, int N, int K,
                        uint8_t* dst, hipStream_t stream);
 hipError_t launch_align(const AlignArgs& a, hipStream_t stream);
 hipError_t launch_build_tiles(const TileBuildArgs& a, hipStream_t stream);
-hipError_t launch_gemm(int kernel, int mt, const GemmArgs& a, int grid, hipStream_t stream);
+// Clears the status words; with a.validate also checks block-derived tiles.
+hipError_t launch_check_blocks(const TileBuildArgs& a, hipStream_t stream);
+// kernel 1 = weight-streaming GEMM.  nt = 16-row weight tiles per wave, mt =
+// 16-row token tiles per work item, wk = waves splitting K, pf = K chunks in
+// flight per wave.
+hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArgs& a, int grid,
+                       hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream);
 

@@ -84,6 +84,7 @@ chord_status check_device(int* cus) {
 struct EnvOverrides {
   int kernel = 0;
   int tokens = 0;
+  int gu_nt = 0, gu_wk = 0, dn_nt = 0, dn_wk = 0;  // "nt,wk" per GEMM
   bool log = false;
 };
 const EnvOverrides& env() {
@@ -91,6 +92,8 @@ const EnvOverrides& env() {
     EnvOverrides o;
     if (const char* s = getenv("CHORD_W4A16_KERNEL")) o.kernel = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_TOKENS")) o.tokens = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_GATE_UP")) sscanf(s, "%d,%d", &o.gu_nt, &o.gu_wk);
+    if (const char* s = getenv("CHORD_W4A16_DOWN")) sscanf(s, "%d,%d", &o.dn_nt, &o.dn_wk);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
     return o;
   }();
@@ -99,10 +102,21 @@ const EnvOverrides& env() {
 
 // ---- planner and plan cache ------------------------------------------------
 struct PlanKey {
-  int mode, T, k, E_g, E_l, H, I, hint, ov_kernel, ov_tokens, cus;
+  int mode, T, k, E_g, E_l, H, I, hint, cus;
+  int ov[7];  // schedule override fields (kernel, tokens, gu_nt, gu_wk, dn_nt, dn_wk, prefetch)
   int64_t rows;
   bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(*this)) == 0; }
 };
+void fill_override(PlanKey& key, const chord_schedule* s) {
+  if (!s) return;
+  key.ov[0] = s->kernel;
+  key.ov[1] = s->tokens;
+  key.ov[2] = s->gate_up_nt;
+  key.ov[3] = s->gate_up_wk;
+  key.ov[4] = s->down_nt;
+  key.ov[5] = s->down_wk;
+  key.ov[6] = s->prefetch;
+}
 struct PlanKeyHash {
   size_t operator()(const PlanKey& k) const {
     const unsigned char* p = reinterpret_cast<const unsigned char*>(&k);
@@ -111,14 +125,21 @@ struct PlanKeyHash {
     return h;
   }
 };
+struct GemmPlan {
+  int kernel;  // 1 weight-streaming
+  int nt;      // 16-row weight tiles per wave
+  int wk;      // waves splitting K
+  int pf;      // K chunks in flight per wave
+  int grid;    // persistent workgroups
+};
 struct Plan {
-  int kernel;       // 1 skinny
-  int mt;           // 16-row token tiles per work item
-  int tile_tokens;  // rows per device tile
-  int nt;           // 16-row weight tiles per work item
+  int mt;            // 16-row token tiles per work item
+  int tile_tokens;   // rows per device tile
+  bool block_tiles;  // indexed: one tile per alignment block (no tile builder)
   int max_tiles;
-  int grid_gate_up, grid_down;
-  char text[160];
+  int cus;
+  GemmPlan gu, dn;
+  char text[200];
 };
 std::mutex g_plan_mu;
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
@@ -131,7 +152,6 @@ int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
 // total token count.
 Plan make_plan(const PlanKey& key) {
   Plan p{};
-  p.kernel = 1;
   double tok_e;
   if (key.mode == kIndexed) {
     const int eg = key.E_g > 0 ? key.E_g : key.E_l;
@@ -142,27 +162,44 @@ Plan make_plan(const PlanKey& key) {
     tok_e = 128.0;
   }
   int mt = (int)((tok_e + 15.0) / 16.0);
-  mt = std::max(1, std::min(4, mt));
-  int kernel = key.ov_kernel ? key.ov_kernel : env().kernel;
-  int tokens = key.ov_tokens ? key.ov_tokens : env().tokens;
-  if (kernel == 1 || kernel == 0) {
-    if (tokens > 0) mt = std::max(1, std::min(4, tokens / 16));
-  }
-  p.kernel = 1;
+  mt = std::max(1, std::min(2, mt));
+  const int tokens = key.ov[1] ? key.ov[1] : env().tokens;
+  if (tokens > 0) mt = std::max(1, std::min(2, tokens / 16));
   p.mt = mt;
+  p.cus = key.cus;
   p.tile_tokens = mt * 16;
-  p.nt = 2;
-  p.max_tiles = max_tiles_for(key.rows, key.E_l, p.tile_tokens);
-  const int n_tiles_gu = 2 * key.I / 16, n_tiles_dn = key.H / 16;
-  const int64_t items_gu = (int64_t)p.max_tiles * (n_tiles_gu / p.nt);
-  const int64_t items_dn = (int64_t)p.max_tiles * (n_tiles_dn / p.nt);
-  const int64_t target = (int64_t)std::max(key.cus, 1) * 8;
-  p.grid_gate_up = (int)std::max<int64_t>(1, std::min(items_gu, target));
-  p.grid_down = (int)std::max<int64_t>(1, std::min(items_dn, target));
+  // key.hint carries block_m for indexed calls.
+  p.block_tiles = key.mode == kIndexed && key.hint == p.tile_tokens;
+  p.max_tiles = p.block_tiles ? (int)((key.rows + key.hint - 1) / key.hint)
+                              : max_tiles_for(key.rows, key.E_l, p.tile_tokens);
+  const int ov_pf = key.ov[6];
+  auto gemm = [&](int N, int K, int ov_nt, int ov_wk, int env_nt, int env_wk) {
+    GemmPlan g{};
+    g.kernel = 1;
+    // Defaults measured on MI355X at the decode / TP-slice shapes: deep-K
+    // gate_up splits K over two waves; the short-K down GEMM runs one wave per
+    // item with 4 weight tiles; very short K (<= 512) keeps 4 chunks in flight.
+    const int chunks = K / kChunkK;
+    g.nt = 4;
+    g.wk = chunks >= 24 ? 2 : 1;
+    g.pf = chunks <= 4 ? 4 : 2;
+    const int nt = ov_nt ? ov_nt : env_nt;
+    const int wk = ov_wk ? ov_wk : env_wk;
+    if (nt == 2 || nt == 4) g.nt = nt;
+    if (wk == 1 || wk == 2 || wk == 4) g.wk = wk;
+    if (ov_pf == 2 || ov_pf == 4) g.pf = ov_pf;
+    if ((N / 16) % g.nt != 0) g.nt = 2;
+    const int64_t items = (int64_t)p.max_tiles * ((N / 16) / g.nt);
+    g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)key.cus * 64));
+    return g;
+  };
+  p.gu = gemm(2 * key.I, key.H, key.ov[2], key.ov[3], env().gu_nt, env().gu_wk);
+  p.dn = gemm(key.H, key.I, key.ov[4], key.ov[5], env().dn_nt, env().dn_wk);
   snprintf(p.text, sizeof(p.text),
-           "kernel=skinny mt=%d tile_tokens=%d nt=%d wk=4 max_tiles=%d grid_gu=%d grid_dn=%d "
-           "tok_e=%.1f",
-           p.mt, p.tile_tokens, p.nt, p.max_tiles, p.grid_gate_up, p.grid_down, tok_e);
+           "tok_e=%.1f tile_tokens=%d tiles=%s max_tiles=%d | gate_up stream nt=%d mt=%d wk=%d "
+           "pf=%d | down stream nt=%d mt=%d wk=%d pf=%d",
+           tok_e, p.tile_tokens, p.block_tiles ? "blocks" : "list", p.max_tiles, p.gu.nt, p.mt,
+           p.gu.wk, p.gu.pf, p.dn.nt, p.mt, p.dn.wk, p.dn.pf);
   return p;
 }
 
@@ -291,11 +328,17 @@ void set_plan_text(const char* mode, const Plan& p) {
 // Shared GEMM sequence: tiles -> gate_up -> down.
 chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, uint8_t* wsp,
                               const chord_w4a16_weight* w13, const chord_w4a16_weight* w2, int H,
-                              int I, const uint16_t* bsrc, int64_t rows_internal,
-                              const int32_t* sorted_ids, int topk, int64_t n_flat,
-                              const int32_t* m_indices, uint16_t* down_out, int64_t down_rows,
-                              const float* row_weights, TileBuildArgs tb, hipStream_t stream,
-                              StageTimer& timer) {
+                              int I, const uint16_t* bsrc, int64_t bsrc_rows,
+                              int64_t rows_internal, const int32_t* sorted_ids, int topk,
+                              int64_t n_flat, const int32_t* m_indices, uint16_t* down_out,
+                              int64_t down_rows, const float* row_weights, TileBuildArgs tb,
+                              hipStream_t stream, StageTimer& timer) {
+  // Buffer resources address their source with 32-bit offsets.
+  const int64_t kMaxBuf = ((int64_t)1 << 31) - 1;
+  if (bsrc_rows * H * 2 > kMaxBuf || rows_internal * I * 2 > kMaxBuf ||
+      (int64_t)(2 * I / kTileRows) * (H / kChunkK) * kBlockBytes > kMaxBuf ||
+      (int64_t)(H / kTileRows) * (I / kChunkK) * kBlockBytes > kMaxBuf)
+    return fail(CHORD_ERR_UNSUPPORTED, "a layer operand exceeds 2 GiB");
   DevStatus* status = reinterpret_cast<DevStatus*>(wsp + ws.status);
   TileDesc* tiles = reinterpret_cast<TileDesc*>(wsp + ws.tiles);
   uint16_t* h = reinterpret_cast<uint16_t*>(wsp + ws.h);
@@ -305,7 +348,11 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   tb.tiles = tiles;
   tb.status = status;
   timer.mark(0);
-  HIP_TRY(launch_build_tiles(tb, stream), "tile builder launch");
+  if (plan.block_tiles) {
+    HIP_TRY(launch_check_blocks(tb, stream), "block check launch");
+  } else {
+    HIP_TRY(launch_build_tiles(tb, stream), "tile builder launch");
+  }
   timer.mark(1);
 
   GemmArgs g{};
@@ -314,10 +361,15 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.topk = topk;
   g.n_flat = n_flat;
   g.m_indices = m_indices;
-  g.tiles = tiles;
+  g.tiles = plan.block_tiles ? nullptr : tiles;
   g.status = status;
+  g.expert_ids = tb.expert_ids;
+  g.ntpp = tb.ntpp;
+  g.block_m = tb.block_m;
+  g.max_padded = tb.max_padded;
+  g.num_experts = tb.num_experts;
+  g.num_cus = plan.cus;
   g.tile_tokens = plan.tile_tokens;
-  g.tiles_per_item = plan.nt;
   g.n_rows_internal = rows_internal;
 
   // gate_up: B = activations rows, out = h [rows_internal, I]
@@ -326,13 +378,17 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.n_chunks = H / kChunkK;
   g.K = H;
   g.bsrc = bsrc;
+  g.bsrc_bytes = bsrc_rows * H * 2;
   g.gate_up = 1;
-  g.items_per_tile = g.n_tiles / plan.nt;
+  g.tiles_per_item = plan.gu.nt;
+  g.items_per_tile = g.n_tiles / plan.gu.nt;
   g.out = h;
   g.out_ld = I;
   g.out_rows = rows_internal;
   g.row_weights = nullptr;
-  HIP_TRY(launch_gemm(plan.kernel, plan.mt, g, plan.grid_gate_up, stream), "gate_up launch");
+  HIP_TRY(launch_gemm(plan.gu.kernel, plan.gu.nt, plan.mt, plan.gu.wk, plan.gu.pf, g,
+                      plan.gu.grid, stream),
+          "gate_up launch");
   timer.mark(2);
 
   // down: B = h, out = y / out rows
@@ -341,13 +397,17 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.n_chunks = I / kChunkK;
   g.K = I;
   g.bsrc = h;
+  g.bsrc_bytes = rows_internal * I * 2;
   g.gate_up = 0;
-  g.items_per_tile = g.n_tiles / plan.nt;
+  g.tiles_per_item = plan.dn.nt;
+  g.items_per_tile = g.n_tiles / plan.dn.nt;
   g.out = down_out;
   g.out_ld = H;
   g.out_rows = down_rows;
   g.row_weights = row_weights;
-  HIP_TRY(launch_gemm(plan.kernel, plan.mt, g, plan.grid_down, stream), "down launch");
+  HIP_TRY(launch_gemm(plan.dn.kernel, plan.dn.nt, plan.mt, plan.dn.wk, plan.dn.pf, g,
+                      plan.dn.grid, stream),
+          "down launch");
   timer.mark(3);
   return CHORD_OK;
 }
@@ -532,8 +592,12 @@ chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_b
 }
 
 int chord_w4a16_moe_indexed_block_m(int T, int k, int E_g, int E_l, int H, int I) {
-  (void)T; (void)k; (void)E_g; (void)E_l; (void)H; (void)I;
-  return 16;
+  (void)H; (void)I;
+  // Expected rows per expert under uniform routing; a block of 16 or 32 rows
+  // is then one tile of the weight-streaming GEMM.
+  const int eg = E_g > 0 ? E_g : (E_l > 0 ? E_l : 1);
+  const double tok_e = (double)std::max(T, 0) * std::max(k, 0) / eg;
+  return (tok_e > 16.0 && tok_e <= 32.0) ? 32 : 16;
 }
 
 size_t chord_w4a16_moe_workspace_bytes(int mode, int T, int k, int E_l, int H, int I,
@@ -566,17 +630,25 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
                 (long long)max_padded);
   if ((int64_t)T * k >= ((int64_t)1 << 30) || max_padded >= ((int64_t)1 << 31))
     return fail(CHORD_ERR_UNSUPPORTED, "routing tensors too large");
-  if (override && (override->kernel < 0 || override->kernel > 1 || override->tokens < 0 ||
-                   override->tokens % 16 != 0 || override->tokens > 64))
-    return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
+  if (override) {
+    auto in = [](int v, std::initializer_list<int> ok) {
+      for (int o : ok)
+        if (v == o) return true;
+      return false;
+    };
+    if (!in(override->kernel, {0, 1}) || !in(override->tokens, {0, 16, 32}) ||
+        !in(override->gate_up_nt, {0, 2, 4}) || !in(override->down_nt, {0, 2, 4}) ||
+        !in(override->gate_up_wk, {0, 1, 2, 4}) || !in(override->down_wk, {0, 1, 2, 4}) ||
+        !in(override->prefetch, {0, 2, 4}))
+      return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
+  }
   const WsLayout ws = layer_ws(kIndexed, T, k, E_l, H, I, max_padded);
   if (!workspace || ws_bytes < ws.total)
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
   int cus = 0;
   CHORD_CHECK(check_device(&cus));
-  const PlanKey key{kIndexed, T, k, num_global_experts, E_l, H, I, block_m,
-                    override ? override->kernel : 0, override ? override->tokens : 0, cus,
-                    max_padded};
+  PlanKey key{kIndexed, T, k, num_global_experts, E_l, H, I, block_m, cus, {0}, max_padded};
+  fill_override(key, override);
   const Plan plan = get_plan(key);
   set_plan_text("indexed", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -590,9 +662,9 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
   tb.max_padded = max_padded;
   uint16_t* y = reinterpret_cast<uint16_t*>(wsp + ws.y);
   StageTimer timer(st);
-  CHORD_CHECK(run_expert_gemms(kIndexed, plan, ws, wsp, w13, w2, H, I, x, max_padded, sorted_ids,
-                               k, (int64_t)T * k, nullptr, y, (int64_t)T * k, nullptr, tb, st,
-                               timer));
+  CHORD_CHECK(run_expert_gemms(kIndexed, plan, ws, wsp, w13, w2, H, I, x, T, max_padded,
+                               sorted_ids, k, (int64_t)T * k, nullptr, y, (int64_t)T * k, nullptr,
+                               tb, st, timer));
   CombineArgs c{};
   c.rows = y;
   c.topk_ids = topk_ids;
@@ -642,7 +714,7 @@ chord_status chord_w4a16_moe_grouped_contiguous(
   int cus = 0;
   CHORD_CHECK(check_device(&cus));
   const PlanKey key{kContiguous, T, k, 0, E_l, H, I, (int)std::min<int64_t>(valid_m_hint, 1 << 30),
-                    0, 0, cus, M};
+                    cus, {0}, M};
   const Plan plan = get_plan(key);
   set_plan_text("contiguous", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -653,7 +725,7 @@ chord_status chord_w4a16_moe_grouped_contiguous(
   tb.m_indices = m_indices;
   tb.M = M;
   StageTimer timer(st);
-  CHORD_CHECK(run_expert_gemms(kContiguous, plan, ws, wsp, w13, w2, H, I, a, M, nullptr, 1, 0,
+  CHORD_CHECK(run_expert_gemms(kContiguous, plan, ws, wsp, w13, w2, H, I, a, M, M, nullptr, 1, 0,
                                m_indices, out_rows, M, row_weights, tb, st, timer));
   if (want_tokens && T > 0) {
     CombineArgs c{};
@@ -702,7 +774,7 @@ chord_status chord_w4a16_moe_grouped_masked(const chord_bf16* a, int E, int max_
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
   int cus = 0;
   CHORD_CHECK(check_device(&cus));
-  const PlanKey key{kMasked, 0, 0, 0, E, H, I, expected_m, 0, 0, cus, rows};
+  const PlanKey key{kMasked, 0, 0, 0, E, H, I, expected_m, cus, {0}, rows};
   const Plan plan = get_plan(key);
   set_plan_text("masked", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -713,8 +785,8 @@ chord_status chord_w4a16_moe_grouped_masked(const chord_bf16* a, int E, int max_
   tb.masked_m = masked_m;
   tb.max_m = max_m;
   StageTimer timer(st);
-  CHORD_CHECK(run_expert_gemms(kMasked, plan, ws, wsp, w13, w2, H, I, a, rows, nullptr, 1, 0,
-                               nullptr, out, rows, row_weights, tb, st, timer));
+  CHORD_CHECK(run_expert_gemms(kMasked, plan, ws, wsp, w13, w2, H, I, a, rows, rows, nullptr, 1,
+                               0, nullptr, out, rows, row_weights, tb, st, timer));
   timer.mark(4);
   timer.finish();
   return finish_validate(flags, ws, wsp, st);

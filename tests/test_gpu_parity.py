@@ -118,7 +118,7 @@ def test_indexed_small_shapes(T, H, I, E_g, E_l, k, eb):
     check_close(got, ref)
 
 
-@pytest.mark.parametrize("tokens", [16, 32, 48, 64])
+@pytest.mark.parametrize("tokens", [16, 32])
 def test_indexed_schedule_overrides_bit_identical(tokens):
     """Schedules differ only in tiling of tokens: results must be bit-identical."""
     banner(f"indexed schedule override tokens={tokens}")
