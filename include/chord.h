@@ -97,8 +97,11 @@ typedef struct {
  * Grouped entry points reject any override ([Novita] §"Gruppierte SM90-Kernel":
  * the grouped dispatch does not accept indexed block_m / tuning overrides). */
 typedef struct {
-  int32_t kernel;      /* 0 auto, 1 weight-streaming GEMMs */
-  int32_t tokens;      /* rows per token tile: 16 or 32; 0 auto */
+  int32_t kernel;      /* 0 auto, 1 weight-streaming GEMMs, 2 LDS-tiled GEMMs (needs
+                          2*I and H multiples of 256, else kernel 1 runs; tiles of
+                          128 token rows; the nt/wk/prefetch/tokens fields are
+                          then ignored) */
+  int32_t tokens;      /* rows per token tile of kernel 1: 16 or 32; 0 auto */
   int32_t gate_up_nt;  /* 16-row weight tiles per wave in the gate_up GEMM: 2 or 4; 0 auto */
   int32_t gate_up_wk;  /* waves splitting K in the gate_up GEMM: 1, 2 or 4; 0 auto */
   int32_t down_nt;     /* as above for the down GEMM */

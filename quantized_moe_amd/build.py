@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libchord.so")
-SOURCES = ["runtime.cpp", "align.hip", "pack.hip", "moe_kernels.hip", "gemm_stream.hip"]
+SOURCES = ["runtime.cpp", "align.hip", "pack.hip", "moe_kernels.hip", "gemm_stream.hip",
+           "gemm_tile.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -56,10 +56,12 @@ struct TileDesc {
 enum Layout : int { kIndexed = 0, kContiguous = 1, kMasked = 2 };
 
 // Device status words at the start of every layer workspace.
+constexpr int kTileGroups = 8;  // tiles are grouped by expert % 8 (one group per XCD)
 struct DevStatus {
-  int32_t error;   // nonzero: routing validation failed (bit flags)
-  int32_t ntiles;  // tiles written by the tile builder
-  int32_t pad[62];
+  int32_t error;                        // nonzero: routing validation failed (bit flags)
+  int32_t ntiles;                       // tiles written by the tile builder
+  int32_t group_start[kTileGroups + 1]; // tile range of each expert group
+  int32_t pad[53];
 };
 
 // Arguments of the tile builder (one workgroup).
@@ -159,6 +161,9 @@ hipError_t launch_check_blocks(const TileBuildArgs& a, hipStream_t stream);
 // flight per wave.
 hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArgs& a, int grid,
                        hipStream_t stream);
+// LDS-tiled GEMM (needs a device tile list; 4 weight tiles per wave, 256 rows
+// per workgroup, so N must be a multiple of 256).  mt = 8 or 16 token groups.
+hipError_t launch_gemm_tile(int mt, const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream);
 

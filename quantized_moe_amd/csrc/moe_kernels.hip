@@ -33,12 +33,12 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
   }
   __syncthreads();
 
-  int my_tiles = 0;
+  // Pass 0: per-expert extents (indexed) / counts (masked), with validation.
   if (a.layout == kIndexed) {
     int64_t ntpp = *a.ntpp;
     const int64_t nb_cap = (a.max_padded + a.block_m - 1) / a.block_m;
     if (ntpp < 0 || ntpp > a.max_padded || ntpp % a.block_m != 0) {
-      if (a.validate) atomicOr(&err, 4);
+      if (a.validate && tid == 0) atomicOr(&err, 4);
       ntpp = ntpp < 0 ? 0 : (ntpp > a.max_padded ? a.max_padded : ntpp);
     }
     const int64_t nb = min(ntpp / a.block_m, nb_cap);
@@ -53,70 +53,78 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
       atomicAdd(&nblk[e], 1);
     }
     __syncthreads();
-    if (tid < E && last[tid] >= 0) {
-      const int nbk = last[tid] - first[tid] + 1;
-      if (nbk != nblk[tid] && a.validate) atomicOr(&err, 2);
-      my_tiles = (nbk * a.block_m + TOK - 1) / TOK;
-    }
+    if (tid < E && last[tid] >= 0 && a.validate && last[tid] - first[tid] + 1 != nblk[tid])
+      atomicOr(&err, 2);
   } else if (a.layout == kMasked) {
     if (tid < E) {
       int m = a.masked_m[tid];
       if ((m < 0 || m > a.max_m) && a.validate) atomicOr(&err, 32);
       m = m < 0 ? 0 : (m > a.max_m ? a.max_m : m);
       first[tid] = m;  // rows
-      my_tiles = (m + TOK - 1) / TOK;
-    }
-  } else {
-    // contiguous: thread handles chunks [c0, c1)
-    const int nch = (int)(a.M / 128);
-    const int per = (nch + blockDim.x - 1) / blockDim.x;
-    const int c0 = tid * per, c1 = min(nch, c0 + per);
-    for (int c = c0; c < c1; ++c) {
-      const int e = a.m_indices[(int64_t)c * 128];
-      if (e < 0 || e >= E) {
-        if (e != -1 && a.validate) atomicOr(&err, 8);
-        continue;
-      }
-      int lastv = 0;
-      for (int r = 0; r < 128; ++r) {
-        const int v = a.m_indices[(int64_t)c * 128 + r];
-        if (v == e) lastv = r + 1;
-        else if (a.validate && v != -1) atomicOr(&err, (v < -1 || v >= E) ? 8 : 16);
-      }
-      my_tiles += (lastv + TOK - 1) / TOK;
-    }
-  }
-  int total;
-  int base = block_scan_excl(my_tiles, tmp, &total);
-  if (total > a.max_tiles && a.validate) atomicOr(&err, 64);
-
-  auto emit = [&](int expert, int row_begin, int rows) {
-    for (int r = 0; r < rows; r += TOK) {
-      if (base < a.max_tiles) a.tiles[base] = TileDesc{expert, row_begin + r, min(TOK, rows - r), 0};
-      ++base;
-    }
-  };
-  if (a.layout == kIndexed) {
-    if (tid < E && last[tid] >= 0)
-      emit(tid, first[tid] * a.block_m, (last[tid] - first[tid] + 1) * a.block_m);
-  } else if (a.layout == kMasked) {
-    if (tid < E && first[tid] > 0) emit(tid, tid * a.max_m, first[tid]);
-  } else {
-    const int nch = (int)(a.M / 128);
-    const int per = (nch + blockDim.x - 1) / blockDim.x;
-    const int c0 = tid * per, c1 = min(nch, c0 + per);
-    for (int c = c0; c < c1; ++c) {
-      const int e = a.m_indices[(int64_t)c * 128];
-      if (e < 0 || e >= E) continue;
-      int lastv = 0;
-      for (int r = 0; r < 128; ++r)
-        if (a.m_indices[(int64_t)c * 128 + r] == e) lastv = r + 1;
-      emit(e, c * 128, lastv);
     }
   }
   __syncthreads();
+
+  // Segments owned by this thread: one expert (indexed, masked) or a range of
+  // 128-row chunks (contiguous).  f(expert, row_begin, rows).
+  const int nch = (int)(a.M / 128);
+  const int per = (nch + blockDim.x - 1) / blockDim.x;
+  auto for_each_segment = [&](auto&& f, bool check) {
+    if (a.layout == kIndexed) {
+      if (tid < E && last[tid] >= 0)
+        f(tid, first[tid] * a.block_m, (last[tid] - first[tid] + 1) * a.block_m);
+    } else if (a.layout == kMasked) {
+      if (tid < E && first[tid] > 0) f(tid, tid * a.max_m, first[tid]);
+    } else {
+      const int c0 = tid * per, c1 = min(nch, c0 + per);
+      for (int c = c0; c < c1; ++c) {
+        const int e = a.m_indices[(int64_t)c * 128];
+        if (e < 0 || e >= E) {
+          if (check && e != -1 && a.validate) atomicOr(&err, 8);
+          continue;
+        }
+        int lastv = 0;
+        for (int r = 0; r < 128; ++r) {
+          const int v = a.m_indices[(int64_t)c * 128 + r];
+          if (v == e) lastv = r + 1;
+          else if (check && a.validate && v != -1) atomicOr(&err, (v < -1 || v >= E) ? 8 : 16);
+        }
+        f(e, c * 128, lastv);
+      }
+    }
+  };
+
+  // Count tiles per expert group (expert % 8), scan each group, emit tiles
+  // group-major so that one XCD can take all tiles of its experts.
+  int cnt[kTileGroups];
+#pragma unroll
+  for (int g = 0; g < kTileGroups; ++g) cnt[g] = 0;
+  for_each_segment([&](int e, int, int rows) { cnt[e % kTileGroups] += (rows + TOK - 1) / TOK; },
+                   true);
+  int base[kTileGroups];
+  int gstart = 0;
+#pragma unroll
+  for (int g = 0; g < kTileGroups; ++g) {
+    int tot;
+    base[g] = gstart + block_scan_excl(cnt[g], tmp, &tot);
+    if (tid == 0) a.status->group_start[g] = min(gstart, a.max_tiles);
+    gstart += tot;
+  }
+  const int total = gstart;
+  if (total > a.max_tiles && a.validate && tid == 0) atomicOr(&err, 64);
+  for_each_segment(
+      [&](int e, int row_begin, int rows) {
+        int& b = base[e % kTileGroups];
+        for (int r = 0; r < rows; r += TOK) {
+          if (b < a.max_tiles) a.tiles[b] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0};
+          ++b;
+        }
+      },
+      false);
+  __syncthreads();
   if (tid == 0) {
     a.status->ntiles = min(total, a.max_tiles);
+    a.status->group_start[kTileGroups] = min(total, a.max_tiles);
     a.status->error = err;
   }
 }

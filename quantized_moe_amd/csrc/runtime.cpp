@@ -85,6 +85,7 @@ struct EnvOverrides {
   int kernel = 0;
   int tokens = 0;
   int gu_nt = 0, gu_wk = 0, dn_nt = 0, dn_wk = 0;  // "nt,wk" per GEMM
+  int tile_wgs = 0;  // tiled kernel: workgroups per CU
   bool log = false;
 };
 const EnvOverrides& env() {
@@ -94,6 +95,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_TOKENS")) o.tokens = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_GATE_UP")) sscanf(s, "%d,%d", &o.gu_nt, &o.gu_wk);
     if (const char* s = getenv("CHORD_W4A16_DOWN")) sscanf(s, "%d,%d", &o.dn_nt, &o.dn_wk);
+    if (const char* s = getenv("CHORD_W4A16_TILE_WGS")) o.tile_wgs = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
     return o;
   }();
@@ -133,6 +135,7 @@ struct GemmPlan {
   int grid;    // persistent workgroups
 };
 struct Plan {
+  int kernel;        // 1 weight-streaming GEMMs, 2 LDS-tiled GEMMs
   int mt;            // 16-row token tiles per work item
   int tile_tokens;   // rows per device tile
   bool block_tiles;  // indexed: one tile per alignment block (no tile builder)
@@ -143,6 +146,10 @@ struct Plan {
 };
 std::mutex g_plan_mu;
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
+
+constexpr int kTileSlice = 256;    // output rows per workgroup of the tiled kernel
+constexpr int kTileTokens = 128;   // token rows per tile of the tiled kernel
+constexpr double kTileMinRows = 48.0;
 
 int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
   return (int)((rows + tile_tokens - 1) / tile_tokens) + E_l + 1;
@@ -161,12 +168,45 @@ Plan make_plan(const PlanKey& key) {
   } else {
     tok_e = 128.0;
   }
+  p.cus = key.cus;
+  // Kernel family: the LDS-tiled kernel once an expert's rows can amortise
+  // the in-register dequantisation over many MFMAs (and N fits its 256-row
+  // slices); the weight-streaming kernel below that.
+  const bool tile_ok = (2 * key.I) % kTileSlice == 0 && key.H % kTileSlice == 0;
+  int kernel = key.ov[0] ? key.ov[0] : env().kernel;
+  if (kernel != 1 && kernel != 2) kernel = (tile_ok && tok_e >= kTileMinRows) ? 2 : 1;
+  if (kernel == 2 && !tile_ok) kernel = 1;
+  p.kernel = kernel;
+  if (kernel == 2) {
+    p.mt = kTileTokens / 16;
+    p.tile_tokens = kTileTokens;
+    p.block_tiles = false;
+    p.max_tiles = max_tiles_for(key.rows, key.E_l, p.tile_tokens);
+    auto tgemm = [&](int N) {
+      GemmPlan g{};
+      g.kernel = 2;
+      g.nt = 4;
+      g.wk = 1;
+      g.pf = 2;
+      const int64_t items = (int64_t)p.max_tiles * (N / kTileSlice);
+      // Two 71 KB-LDS workgroups fit one CU; the launcher clamps to occupancy.
+      const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 2;
+      g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
+      return g;
+    };
+    p.gu = tgemm(2 * key.I);
+    p.dn = tgemm(key.H);
+    snprintf(p.text, sizeof(p.text),
+             "tok_e=%.1f tile_tokens=%d tiles=list max_tiles=%d | gate_up tile 256x%d | down tile "
+             "256x%d",
+             tok_e, p.tile_tokens, p.max_tiles, p.tile_tokens, p.tile_tokens);
+    return p;
+  }
   int mt = (int)((tok_e + 15.0) / 16.0);
   mt = std::max(1, std::min(2, mt));
   const int tokens = key.ov[1] ? key.ov[1] : env().tokens;
-  if (tokens > 0) mt = std::max(1, std::min(2, tokens / 16));
+  if (tokens == 16 || tokens == 32) mt = tokens / 16;
   p.mt = mt;
-  p.cus = key.cus;
   p.tile_tokens = mt * 16;
   // key.hint carries block_m for indexed calls.
   p.block_tiles = key.mode == kIndexed && key.hint == p.tile_tokens;
@@ -325,6 +365,18 @@ void set_plan_text(const char* mode, const Plan& p) {
   g_last_plan = b;
 }
 
+// Launches one expert GEMM with its planned kernel.
+hipError_t launch_planned(const GemmPlan& gp, int mt, GemmArgs& g, hipStream_t stream) {
+  if (gp.kernel == 2) {
+    g.tiles_per_item = kTileSlice / kTileRows;
+    g.items_per_tile = g.n_tiles / g.tiles_per_item;
+    return launch_gemm_tile(mt, g, gp.grid, stream);
+  }
+  g.tiles_per_item = gp.nt;
+  g.items_per_tile = g.n_tiles / gp.nt;
+  return launch_gemm(gp.kernel, gp.nt, mt, gp.wk, gp.pf, g, gp.grid, stream);
+}
+
 // Shared GEMM sequence: tiles -> gate_up -> down.
 chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, uint8_t* wsp,
                               const chord_w4a16_weight* w13, const chord_w4a16_weight* w2, int H,
@@ -380,15 +432,11 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.bsrc = bsrc;
   g.bsrc_bytes = bsrc_rows * H * 2;
   g.gate_up = 1;
-  g.tiles_per_item = plan.gu.nt;
-  g.items_per_tile = g.n_tiles / plan.gu.nt;
   g.out = h;
   g.out_ld = I;
   g.out_rows = rows_internal;
   g.row_weights = nullptr;
-  HIP_TRY(launch_gemm(plan.gu.kernel, plan.gu.nt, plan.mt, plan.gu.wk, plan.gu.pf, g,
-                      plan.gu.grid, stream),
-          "gate_up launch");
+  HIP_TRY(launch_planned(plan.gu, plan.mt, g, stream), "gate_up launch");
   timer.mark(2);
 
   // down: B = h, out = y / out rows
@@ -399,15 +447,11 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.bsrc = h;
   g.bsrc_bytes = rows_internal * I * 2;
   g.gate_up = 0;
-  g.tiles_per_item = plan.dn.nt;
-  g.items_per_tile = g.n_tiles / plan.dn.nt;
   g.out = down_out;
   g.out_ld = H;
   g.out_rows = down_rows;
   g.row_weights = row_weights;
-  HIP_TRY(launch_gemm(plan.dn.kernel, plan.dn.nt, plan.mt, plan.dn.wk, plan.dn.pf, g,
-                      plan.dn.grid, stream),
-          "down launch");
+  HIP_TRY(launch_planned(plan.dn, plan.mt, g, stream), "down launch");
   timer.mark(3);
   return CHORD_OK;
 }
@@ -636,7 +680,7 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
         if (v == o) return true;
       return false;
     };
-    if (!in(override->kernel, {0, 1}) || !in(override->tokens, {0, 16, 32}) ||
+    if (!in(override->kernel, {0, 1, 2}) || !in(override->tokens, {0, 16, 32}) ||
         !in(override->gate_up_nt, {0, 2, 4}) || !in(override->down_nt, {0, 2, 4}) ||
         !in(override->gate_up_wk, {0, 1, 2, 4}) || !in(override->down_wk, {0, 1, 2, 4}) ||
         !in(override->prefetch, {0, 2, 4}))

@@ -360,3 +360,40 @@ def test_masked_zipf_full_size_sampled(E_l):
         ref = oracle.grouped_masked(sub, np.array([len(rows)], np.int32), wl.q13[e:e + 1],
                                     wl.s13[e:e + 1], wl.q2[e:e + 1], wl.s2[e:e + 1])
         check_close(got[[e * wl.max_m + r for r in rows]], ref, f"masked e={e}")
+
+
+# ---------------------------------------------------------------------------
+# LDS-tiled kernel (many rows per expert)
+# ---------------------------------------------------------------------------
+
+def test_tile_kernel_bit_identical_to_streaming_kernel():
+    """With one wave per K range both kernels accumulate every output over the
+    same chunks and MFMA steps in the same order, so they must agree bit for
+    bit; several 128-row tiles per expert and ragged tails."""
+    banner("tile kernel vs streaming kernel: indexed T=300 H=512 I=256")
+    case = small_case(301, 300, 512, 256, 16, 8, 4, 4)
+    tiled, layer, _ = run_indexed(*case, E_g=16, bm=16, override={"kernel": 2})
+    stream, _, _ = run_indexed(*case, E_g=16, bm=16, layer=layer,
+                               override={"kernel": 1, "gate_up_wk": 1, "down_wk": 1})
+    assert np.array_equal(tiled, stream)
+    check_close(tiled, oracle.moe_layer(*case))
+
+
+def test_tile_kernel_masked_tile_boundaries():
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("tile kernel: masked rows at tile boundaries")
+    rng = np.random.default_rng(34)
+    E, max_m, H, I = 6, 300, 256, 256
+    a3, _, _, _ = G.draw_masked(rng, E, max_m, H)
+    mm = np.array([0, 1, 128, 129, 300, 255], np.int32)
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H)
+    q2, s2 = G.draw_weights(rng, E, H, I)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_MASKED)
+    out = layer.masked(dev_bf16(a3), dev(mm), 200)   # hint >= 48 rows: tiled kernel
+    torch.cuda.synchronize()
+    assert "tile" in C.last_plan()
+    got = host_bf16(out)
+    ref = oracle.grouped_masked(a3, mm, q13, s13, q2, s2)
+    for e in range(E):
+        sl = slice(e * max_m, e * max_m + mm[e])
+        check_close(got[sl], ref[sl], f"masked e={e}")
