@@ -98,8 +98,8 @@ typedef struct {
  * the grouped dispatch does not accept indexed block_m / tuning overrides). */
 typedef struct {
   int32_t kernel;      /* 0 auto, 1 weight-streaming GEMMs, 2 LDS-tiled GEMMs (needs
-                          2*I and H multiples of 256, else kernel 1 runs; tiles of
-                          128 token rows; the nt/wk/prefetch/tokens fields are
+                          I a multiple of 32, else kernel 1 runs; tiles of up to
+                          192 token rows; the nt/wk/prefetch/tokens fields are
                           then ignored) */
   int32_t tokens;      /* rows per token tile of kernel 1: 16 or 32; 0 auto */
   int32_t gate_up_nt;  /* 16-row weight tiles per wave in the gate_up GEMM: 2 or 4; 0 auto */

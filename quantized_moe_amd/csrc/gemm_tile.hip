@@ -1,26 +1,33 @@
 // LDS-tiled expert GEMM for many rows per expert (prefill, contiguous
 // segments, hot masked experts): MFMA-bound, so every dequantised weight is
-// reused by up to 256 token rows.
+// reused by up to 192 token rows.
 //
-// Workgroup = 4 waves; wave w owns 4 consecutive 16-row weight tiles (64
-// output rows), the workgroup 256 output rows of one expert.  A token tile of
-// up to MT*16 rows is staged in LDS one 128-wide K chunk at a time (double
-// buffer, one barrier per chunk); each wave streams its weight tiles straight
-// from HBM into registers two chunks ahead, dequantises them exactly
-// (bf16_rne((q - 8) * s), same scheme as the streaming kernel) and issues
+// Workgroup = 4 waves (one per SIMD); wave w owns 4 consecutive 16-row weight
+// tiles (64 output rows), the workgroup a 256-row slice of one expert's
+// output.  A token tile of up to 192 rows is staged in LDS one 128-wide K
+// chunk at a time (double buffer, one barrier per chunk).  Each wave streams
+// its weight tiles straight from HBM into registers two chunks ahead,
+// dequantises them exactly (bf16_rne((q - 8) * s)) and issues
 // v_mfma_f32_16x16x32_bf16 with the weights as A and the staged tokens as B.
-// Work items are (token tile, 256-row slice); the 256-row slices of one token
-// tile run on one XCD so its L2 serves the staged token rows.
+// The number of live 16-row token groups of a tile selects a compile-time
+// variant, so the chunk body is one branch-free block in which the
+// dequantisation of MFMA step s+1 is interleaved with the MFMAs of step s.
+// Work items are (token tile, 256-row slice); the slices of one expert run on
+// one XCD so its L2 serves the staged token rows.
 #include "device_common.h"
 
 namespace chord {
 namespace {
 
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr uint32_t kNoRow = 0xC0000000u;
+constexpr uint32_t kNoRow = 0xC0000000u;  // byte offset past any token buffer
 constexpr int kStreamAux = 2;
 constexpr int kXcds = 8;
-constexpr int kRowPitch = kChunkK * 2 + 16;  // LDS bytes per staged token row (padded)
+constexpr int kWaves = 4;
+constexpr int kNT = 4;                        // weight tiles per wave
+constexpr int kMaxGroups = 12;                // 16-row token groups per tile (192 rows)
+constexpr int kXBufBytes = kMaxGroups * 16 * kChunkK * 2;  // one staged K chunk, 192 rows
+constexpr size_t kLdsBytes = 2 * (size_t)kXBufBytes + kMaxGroups * 16 * (4 + 8);
 
 struct DqScale {
   float s, c, s16, c16;
@@ -31,11 +38,14 @@ __device__ __forceinline__ DqScale dq_scale(uint32_t bits16) {
 }
 
 // One packed word (8 codes of one row, inside one scale group) -> 8 bf16.
-__device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, const DqScale& k, uint32_t mlo,
-                                                 uint32_t mhi, uint32_t magic) {
+// Codes read through the fp16 magic 0x6400 | q = 1024 + q (low nibble of a
+// half) or 1024 + 16 q (high nibble), so fma(h, s, -1032 s) and
+// fma(h, s/16, -72 s) give (q - 8) * s exactly; v_cvt_pk_bf16_f32 rounds.
+__device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, const DqScale& k) {
+  const uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
   const uint32_t w8 = w >> 8;
-  const uint32_t m0 = and_or(w, mlo, magic), m1 = and_or(w, mhi, magic);
-  const uint32_t m2 = and_or(w8, mlo, magic), m3 = and_or(w8, mhi, magic);
+  const uint32_t m0 = and_or(w, kMaskLo, kMagic), m1 = and_or(w, kMaskHi, kMagic);
+  const uint32_t m2 = and_or(w8, kMaskLo, kMagic), m3 = and_or(w8, kMaskHi, kMagic);
   const half2_t h0 = __builtin_bit_cast(half2_t, m0), h1 = __builtin_bit_cast(half2_t, m1);
   const half2_t h2 = __builtin_bit_cast(half2_t, m2), h3 = __builtin_bit_cast(half2_t, m3);
   const float f0 = __builtin_fmaf((float)h0[0], k.s, k.c), f1 = __builtin_fmaf((float)h0[1], k.s, k.c);
@@ -46,6 +56,10 @@ __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, const DqScale& k, u
   const float f7 = __builtin_fmaf((float)h3[1], k.s16, k.c16);
   return __builtin_bit_cast(bf16x8_t, make_uint4(pk_bf16(f0, f1), pk_bf16(f2, f3),
                                                  pk_bf16(f4, f5), pk_bf16(f6, f7)));
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int st) {
+  return st == 0 ? v.x : st == 1 ? v.y : st == 2 ? v.z : v.w;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -74,240 +88,242 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
   return m;
 }
 
-// NT = 16-row weight tiles per wave (the workgroup covers 4*NT tiles);
-// MT = maximum 16-row token groups per tile (token tile <= MT*16 rows).
-template <int NT, int MT>
-__global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
-  constexpr int kWaves = 4;
-  constexpr int BM = MT * 16;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* xbuf = smem;                                        // [2][BM][kRowPitch]
-  int32_t* srcoff = reinterpret_cast<int32_t*>(smem + 2 * BM * kRowPitch);  // [BM] byte offsets
-  int64_t* dstrow = reinterpret_cast<int64_t*>(srcoff + BM);   // [BM]
-
+// One work item: token tile of MG live 16-row groups x one 256-row slice.
+// srcoff / dstrow (LDS) already hold the tile's row maps.
+//
+// Token staging goes straight from memory to LDS (buffer_load ... lds): one
+// instruction moves 4 token rows x 256 bytes (one K chunk) into 1 KB of LDS
+// in lane order.  LDS row r holds the row's 16-byte pieces permuted by
+// slot = piece ^ (r % 16); lane l of the instruction for rows 4j..4j+3 fetches
+// piece (l % 16) ^ (r % 16) of row r = 4j + l / 16, so each row is still read
+// as one contiguous 256-byte run, and the MFMA B reads (16 rows, one piece
+// each) hit 16 distinct slots: no bank conflicts.
+template <int MG>
+__device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const int32_t* srcoff,
+                                         const int64_t* dstrow, int e, int ng) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar offsets
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4;
   const int col = lane & 15;
-  const uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const int nc = a.n_chunks;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Wave w issues the DMA instructions j = w + 4 i (rows 4j .. 4j+3).
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
-  const int nslices = a.items_per_tile;  // 256-row slices per expert
-  const int nc = a.n_chunks;
+  const int rsub = 4 * wave + q;                 // row % 16 of this lane's rows
+  const uint32_t pbytes = (uint32_t)((col ^ rsub) * 16);
+  uint32_t voff[MG];
+#pragma unroll
+  for (int i = 0; i < MG; ++i) voff[i] = (uint32_t)srcoff[rsub + 16 * i] + pbytes;
+  auto load_x = [&](int slot, int c) {
+#pragma unroll
+    for (int i = 0; i < MG; ++i) {
+      uint8_t* dst = xbuf + slot * kXBufBytes + (wave + 4 * i) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)dst, 16, voff[i], c * kChunkK * 2, 0, 0);
+    }
+  };
 
-  // XCD-aware item order: the tile list is grouped by expert % 8;
-  // workgroup b runs on XCD b % 8 and takes the tiles of group b % 8 (all
-  // slices), so the token tiles of one expert share that XCD's L2 for its
-  // weight slices.  With fewer than 8 workgroups each takes several groups.
+  // Weights: kNT tiles of the slice per wave.  A wave past the last tile of
+  // a partial slice re-reads the slice's last tiles and stores nothing.
+  const int64_t expert_bytes = (int64_t)a.n_tiles * nc * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+  const int tile0 = (ng * kWaves + wave) * kNT;
+  const bool wave_live = tile0 < a.n_tiles;
+  const int tile_ld = wave_live ? tile0 : a.n_tiles - kNT;
+  uint4 wq[2][kNT];
+  uint32_t sc[2][kNT];
+  auto load_w = [&](int slot, int c) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const uint32_t blk = (uint32_t)((tile_ld + nt) * nc + c) * kBlockBytes;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+      wq[slot][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+      sc[slot][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+    }
+  };
+
+  f32x4_t acc[kNT][MG];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[nt][g] = zero4;
+
+  // B operand of group g, step st: token row g*16 + col, piece q*4 + st.
+  uint32_t boff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ col) * 16));
+
+  // One chunk.  av holds the dequantised step-0 weights on entry; each MFMA
+  // step runs while the next step is dequantised (the last step dequantises
+  // step 0 of the next chunk from the other weight slot, whose loads were
+  // issued at the top of this chunk).  LDS reads of B run two token groups
+  // ahead of their MFMAs.
+  bf16x8_t av[kNT];
+  auto compute = [&](int slot) {
+    const uint8_t* xb = xbuf + slot * kXBufBytes;
+    DqScale ks[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) ks[nt] = dq_scale(sc[slot][nt]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8_t an[kNT];
+      if (st < 3) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) an[nt] = dequant_word(word_of(wq[slot][nt], st + 1), ks[nt]);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          an[nt] = dequant_word(wq[slot ^ 1][nt].x, dq_scale(sc[slot ^ 1][nt]));
+      }
+#pragma unroll
+      for (int g = 0; g < MG; ++g) {
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(xb + boff[st] + g * 16 * 256);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          acc[nt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nt], bv, acc[nt][g], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) av[nt] = an[nt];
+    }
+    // Schedule: two LDS reads up front, then per token group four MFMAs each
+    // followed by a few VALU ops, then the LDS read two groups ahead.
+    constexpr int kValu = (76 + 4 * MG - 1) / (4 * MG);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * MG; ++i) {
+#pragma unroll
+      for (int m = 0; m < kNT; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+      }
+      if (i + 2 < 4 * MG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // Chunk c in buffer `slot`: x(c+1) DMA and weights(c+1) loads into the
+  // other buffer, compute(c), barrier (which waits for this wave's DMA only).
+  // Prefetch indices are clamped instead of guarded so every iteration
+  // issues the same loads (exact wait counts); the clamped re-reads at the
+  // end hit the caches.
+  auto chunk = [&](int slot, int c) {
+    const int cn = c + 1 < nc ? c + 1 : nc - 1;
+    load_x(slot ^ 1, cn);
+    load_w(slot ^ 1, cn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+    compute(slot);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+
+  load_x(0, 0);
+  load_w(0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) av[nt] = dequant_word(wq[0][nt].x, dq_scale(sc[0][nt]));
+  int c = 0;
+  for (; c + 1 < nc; c += 2) {
+    chunk(0, c);
+    chunk(1, c + 1);
+  }
+  if (c < nc) chunk(0, c);
+
+  // Epilogue: lane holds rows 4q..4q+3 of weight tile nt for token col of
+  // group g.
+  if (!wave_live) return;
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    const int64_t dr = dstrow[g * 16 + col];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      if (dr < 0) continue;
+      const f32x4_t v = acc[nt][g];
+      const int tw = tile0 + nt;
+      if (a.gate_up) {
+        const int f0 = tw * 8 + 2 * q;
+        *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
+            pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
+      } else {
+        const int n0 = tw * 16 + 4 * q;
+        const float rw = a.row_weights != nullptr ? a.row_weights[dr] : 1.0f;
+        *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
+            make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* xbuf = smem;                                                  // [2][192][256 B]
+  int32_t* srcoff = reinterpret_cast<int32_t*>(smem + 2 * kXBufBytes);  // [192] byte offsets
+  int64_t* dstrow = reinterpret_cast<int64_t*>(srcoff + kMaxGroups * 16);  // [192]
+  const int tid = threadIdx.x;
+  const int nslices = a.items_per_tile;
+
+  // XCD-aware item order: the tile list is grouped by expert % 8; workgroup
+  // b runs on XCD b % 8 and takes the tiles of group b % 8 (all slices), so
+  // the token rows of one expert stay in that XCD's L2 across its slices.
+  // With fewer than 8 workgroups each takes several groups.
   const int G = gridDim.x < kXcds ? (int)gridDim.x : kXcds;
   const int xg = blockIdx.x % G;
   const int nloc = (gridDim.x + G - 1 - xg) / G;  // workgroups serving xg
   const int lidx = blockIdx.x / G;
 
   for (int g = xg; g < kTileGroups; g += G)
-  for (int j = lidx, t0 = a.status->group_start[g],
-           n_items = (a.status->group_start[g + 1] - t0) * nslices;
-       j < n_items; j += nloc) {
-    const int ti = t0 + j / nslices;
-    const int ng = j % nslices;
-    const TileDesc td = a.tiles[ti];
-    const int e = td.expert;
-    const int nrows = td.nrows < BM ? td.nrows : BM;
-    const int mt_live = (nrows + 15) >> 4;
+    for (int j = lidx, t0 = a.status->group_start[g],
+             n_items = (a.status->group_start[g + 1] - t0) * nslices;
+         j < n_items; j += nloc) {
+      const TileDesc td = a.tiles[t0 + j / nslices];
+      const int ng = j % nslices;
+      const int e = td.expert;
+      const int nrows = td.nrows < kMaxGroups * 16 ? td.nrows : kMaxGroups * 16;
 
-    // Row maps of the token tile.
-    for (int m = tid; m < BM; m += 256) {
-      int32_t so = (int32_t)kNoRow;
-      int64_t dr = -1;
-      if (m < nrows) {
-        const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
-        if (rm.src >= 0) {
-          so = (int32_t)(rm.src * (int64_t)a.K * 2);
-          dr = rm.dst;
-        }
-      }
-      srcoff[m] = so;
-      dstrow[m] = dr;
-    }
-    __syncthreads();
-
-    // Staging: thread tid moves 16-byte pieces (row r, piece p) of the chunk,
-    // in kHalves register batches (two for 256-row tiles to bound registers).
-    constexpr int kPieces = BM * 16 / 256;  // per thread per chunk
-    constexpr int kHalves = MT > 8 ? 2 : 1;
-    constexpr int kBatch = kPieces / kHalves;
-    uint4 xr[kBatch];
-    auto load_x = [&](int c, int h) {
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int idx = tid + 256 * (h * kBatch + i);
-        const int r = idx >> 4, p = idx & 15;
-        const uint32_t off = (uint32_t)srcoff[r];
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xres, off + p * 16, c * kChunkK * 2, 0);
-        xr[i] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
-    };
-    auto store_x = [&](int slot, int h) {
-      uint8_t* base = xbuf + slot * BM * kRowPitch;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int idx = tid + 256 * (h * kBatch + i);
-        const int r = idx >> 4, p = idx & 15;
-        *reinterpret_cast<uint4*>(base + r * kRowPitch + p * 16) = xr[i];
-      }
-    };
-
-    // Weights of this wave: NT tiles of the slice.
-    const int64_t expert_bytes = (int64_t)a.n_tiles * nc * kBlockBytes;
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
-    const int tile0 = (ng * kWaves + wave) * NT;  // first weight tile of this wave
-    uint4 wq[2][NT];
-    uint32_t sc[2][NT];
-    auto load_w = [&](int slot, int c) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t blk = (uint32_t)((tile0 + nt) * nc + c) * kBlockBytes;
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
-        wq[slot][nt] = make_uint4(v[0], v[1], v[2], v[3]);
-        sc[slot][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
-      }
-    };
-
-    f32x4_t acc[NT][MT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = zero4;
-
-    // One chunk: for each MFMA step st, dequantise word st of every weight
-    // tile, then sweep the live token groups (in fours) reading B from LDS.
-    auto compute = [&](int slot, int st_lo, int st_hi) {
-      const uint8_t* xb = xbuf + slot * BM * kRowPitch;
-      DqScale ks[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) ks[nt] = dq_scale(sc[slot][nt]);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if (st < st_lo || st >= st_hi) continue;
-        bf16x8_t av[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const uint32_t w = st == 0 ? wq[slot][nt].x
-                           : st == 1 ? wq[slot][nt].y
-                           : st == 2 ? wq[slot][nt].z : wq[slot][nt].w;
-          av[nt] = dequant_word(w, ks[nt], kMaskLo, kMaskHi, kMagic);
-        }
-        // B operand of token group mt: row mt*16 + col, k = q*32 + st*8.
-        const uint8_t* bp = xb + col * kRowPitch + (q * 32 + st * 8) * 2;
-#pragma unroll
-        for (int g4 = 0; g4 < MT / 4; ++g4) {
-          if (g4 * 4 < mt_live) {
-#pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-              const int mt = g4 * 4 + mm;
-              const bf16x8_t bv =
-                  *reinterpret_cast<const bf16x8_t*>(bp + mt * 16 * kRowPitch);
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt)
-                acc[nt][mt] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nt], bv, acc[nt][mt], 0, 0, 0);
-            }
+      if (tid < kMaxGroups * 16) {  // row maps of the token tile: one row per thread
+        const int m = tid;
+        int32_t so = (int32_t)kNoRow;
+        int64_t dr = -1;
+        if (m < nrows) {
+          const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
+          if (rm.src >= 0) {
+            so = (int32_t)(rm.src * (int64_t)a.K * 2);
+            dr = rm.dst;
           }
         }
+        srcoff[m] = so;
+        dstrow[m] = dr;
       }
-    };
+      __syncthreads();
 
-    // Pipeline: x(c+1) loads -> compute(c) -> weights(c+2) loads ->
-    // x(c+1) to LDS -> barrier.
-#pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
-      load_x(0, h);
-      store_x(0, h);
-    }
-    load_w(0, 0);
-    load_w(1, nc > 1 ? 1 : 0);
-    __syncthreads();
-    // Unrolled by two so the buffer slot is a compile-time index.
-    for (int c0 = 0; c0 < nc; c0 += 2) {
-#pragma unroll
-      for (int slot = 0; slot < 2; ++slot) {
-        const int c = c0 + slot;
-        if (c < nc) {
-          const bool more = c + 1 < nc;
-          if (kHalves == 1) {
-            if (more) load_x(c + 1, 0);
-            compute(slot, 0, 4);
-            if (c + 2 < nc) load_w(slot, c + 2);
-            if (more) store_x(slot ^ 1, 0);
-          } else {
-            if (more) load_x(c + 1, 0);
-            compute(slot, 0, 2);
-            if (more) {
-              store_x(slot ^ 1, 0);
-              load_x(c + 1, 1);
-            }
-            compute(slot, 2, 4);
-            if (c + 2 < nc) load_w(slot, c + 2);
-            if (more) store_x(slot ^ 1, 1);
-          }
-          __syncthreads();
-        }
+      // Live 16-row groups, rounded up to an even count.
+      switch ((nrows + 31) >> 5) {
+        case 0: break;
+        case 1: run_item<2>(a, xbuf, srcoff, dstrow, e, ng); break;
+        case 2: run_item<4>(a, xbuf, srcoff, dstrow, e, ng); break;
+        case 3: run_item<6>(a, xbuf, srcoff, dstrow, e, ng); break;
+        case 4: run_item<8>(a, xbuf, srcoff, dstrow, e, ng); break;
+        case 5: run_item<10>(a, xbuf, srcoff, dstrow, e, ng); break;
+        default: run_item<12>(a, xbuf, srcoff, dstrow, e, ng); break;
       }
+      __syncthreads();  // row maps and LDS reuse by the next item
     }
-
-    // Epilogue: lane holds rows 4q..4q+3 of weight tile nt for token col of
-    // group mt.
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int64_t dr = mt < mt_live ? dstrow[mt * 16 + col] : -1;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (dr < 0) continue;
-        const f32x4_t v = acc[nt][mt];
-        const int tw = tile0 + nt;
-        if (a.gate_up) {
-          const int f0 = tw * 8 + 2 * q;
-          *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
-              pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
-        } else {
-          const int n0 = tw * 16 + 4 * q;
-          const float rw = a.row_weights != nullptr ? a.row_weights[dr] : 1.0f;
-          *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
-              make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
-        }
-      }
-    }
-    __syncthreads();  // row maps and LDS reuse by the next item
-  }
-}
-
-template <int NT, int MT>
-hipError_t launch_tile_t(const GemmArgs& a, int grid, hipStream_t stream) {
-  const size_t lds = (size_t)2 * MT * 16 * kRowPitch + (size_t)MT * 16 * (4 + 8);
-  static const int per_cu = [&] {
-    hipFuncSetAttribute((const void*)gemm_tile<NT, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)lds);
-    return blocks_per_cu(gemm_tile<NT, MT>, 256, lds);
-  }();
-  const int cap = per_cu * (a.num_cus > 0 ? a.num_cus : 256);
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL((gemm_tile<NT, MT>), dim3(grid), dim3(256), lds, stream, a);
-  return hipGetLastError();
 }
 
 }  // namespace
 
-// Tile kernel: weight tiles per wave fixed at 4 (256 rows per workgroup);
-// mt = 16-row token groups per tile (8 or 16).
-hipError_t launch_gemm_tile(int mt, const GemmArgs& a, int grid, hipStream_t stream) {
-  switch (mt) {
-    case 8: return launch_tile_t<4, 8>(a, grid, stream);
-    case 16: return launch_tile_t<4, 16>(a, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream) {
+  static const int per_cu = [] {
+    hipFuncSetAttribute((const void*)gemm_tile, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)kLdsBytes);
+    return blocks_per_cu(gemm_tile, 256, kLdsBytes);
+  }();
+  const int cap = per_cu * (a.num_cus > 0 ? a.num_cus : 256);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(gemm_tile, dim3(grid), dim3(256), kLdsBytes, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace chord

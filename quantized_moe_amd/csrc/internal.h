@@ -161,9 +161,9 @@ hipError_t launch_check_blocks(const TileBuildArgs& a, hipStream_t stream);
 // flight per wave.
 hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArgs& a, int grid,
                        hipStream_t stream);
-// LDS-tiled GEMM (needs a device tile list; 4 weight tiles per wave, 256 rows
-// per workgroup, so N must be a multiple of 256).  mt = 8 or 16 token groups.
-hipError_t launch_gemm_tile(int mt, const GemmArgs& a, int grid, hipStream_t stream);
+// LDS-tiled GEMM (needs a device tile list with tiles of at most 192 rows;
+// 4 weight tiles per wave, 256 output rows per workgroup; N a multiple of 64).
+hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream);
 

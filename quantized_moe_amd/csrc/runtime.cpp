@@ -148,7 +148,7 @@ std::mutex g_plan_mu;
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 
 constexpr int kTileSlice = 256;    // output rows per workgroup of the tiled kernel
-constexpr int kTileTokens = 128;   // token rows per tile of the tiled kernel
+constexpr int kTileTokens = 192;   // token rows per tile of the tiled kernel
 constexpr double kTileMinRows = 48.0;
 
 int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
@@ -172,7 +172,7 @@ Plan make_plan(const PlanKey& key) {
   // Kernel family: the LDS-tiled kernel once an expert's rows can amortise
   // the in-register dequantisation over many MFMAs (and N fits its 256-row
   // slices); the weight-streaming kernel below that.
-  const bool tile_ok = (2 * key.I) % kTileSlice == 0 && key.H % kTileSlice == 0;
+  const bool tile_ok = (2 * key.I) % 64 == 0 && key.H % 64 == 0;  // 4 tiles per wave
   int kernel = key.ov[0] ? key.ov[0] : env().kernel;
   if (kernel != 1 && kernel != 2) kernel = (tile_ok && tok_e >= kTileMinRows) ? 2 : 1;
   if (kernel == 2 && !tile_ok) kernel = 1;
@@ -188,9 +188,10 @@ Plan make_plan(const PlanKey& key) {
       g.nt = 4;
       g.wk = 1;
       g.pf = 2;
-      const int64_t items = (int64_t)p.max_tiles * (N / kTileSlice);
-      // Two 71 KB-LDS workgroups fit one CU; the launcher clamps to occupancy.
-      const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 2;
+      const int64_t items = (int64_t)p.max_tiles * ((N + kTileSlice - 1) / kTileSlice);
+      // One workgroup per CU (registers, ~100 KB of LDS); the launcher clamps
+      // to the occupancy it measures.
+      const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 1;
       g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
       return g;
     };
@@ -369,8 +370,8 @@ void set_plan_text(const char* mode, const Plan& p) {
 hipError_t launch_planned(const GemmPlan& gp, int mt, GemmArgs& g, hipStream_t stream) {
   if (gp.kernel == 2) {
     g.tiles_per_item = kTileSlice / kTileRows;
-    g.items_per_tile = g.n_tiles / g.tiles_per_item;
-    return launch_gemm_tile(mt, g, gp.grid, stream);
+    g.items_per_tile = (g.n_tiles + g.tiles_per_item - 1) / g.tiles_per_item;
+    return launch_gemm_tile(g, gp.grid, stream);
   }
   g.tiles_per_item = gp.nt;
   g.items_per_tile = g.n_tiles / gp.nt;
