@@ -27,7 +27,8 @@ constexpr int kWaves = 4;
 constexpr int kNT = 4;                        // weight tiles per wave
 constexpr int kMaxGroups = 12;                // 16-row token groups per tile (192 rows)
 constexpr int kXBufBytes = kMaxGroups * 16 * kChunkK * 2;  // one staged K chunk, 192 rows
-constexpr size_t kLdsBytes = 2 * (size_t)kXBufBytes + kMaxGroups * 16 * (4 + 8);
+constexpr int kStages = 3;                    // token / weight buffers (two chunks in flight)
+constexpr size_t kLdsBytes = kStages * (size_t)kXBufBytes + kMaxGroups * 16 * (4 + 8);
 
 struct DqScale {
   float s, c, s16, c16;
@@ -134,8 +135,8 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   const int tile0 = (ng * kWaves + wave) * kNT;
   const bool wave_live = tile0 < a.n_tiles;
   const int tile_ld = wave_live ? tile0 : a.n_tiles - kNT;
-  uint4 wq[2][kNT];
-  uint32_t sc[2][kNT];
+  uint4 wq[kStages][kNT];
+  uint32_t sc[kStages][kNT];
   auto load_w = [&](int slot, int c) {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
@@ -157,79 +158,98 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
 #pragma unroll
   for (int st = 0; st < 4; ++st) boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ col) * 16));
 
-  // One chunk.  av holds the dequantised step-0 weights on entry; each MFMA
-  // step runs while the next step is dequantised (the last step dequantises
-  // step 0 of the next chunk from the other weight slot, whose loads were
-  // issued at the top of this chunk).  LDS reads of B run two token groups
-  // ahead of their MFMAs.
+  // One chunk, software-pipelined by hand (scheduling fences keep the order):
+  // the chunk is 4 MFMA steps x MG token groups; each group section issues
+  // the LDS read of the B fragment two groups ahead, the 4 MFMAs of its own
+  // group, and a share of the dequantisation of the next step (weight tile
+  // nt is dequantised in group nt * MG / 4).  av holds the dequantised
+  // weights of the current step; the last step dequantises step 0 of the
+  // next chunk from the weight slot `next`.  B reads do not cross the chunk
+  // boundary: the next chunk's buffer is only valid after the barrier.
   bf16x8_t av[kNT];
-  auto compute = [&](int slot) {
+  auto bread = [&](const uint8_t* xb, int st, int g) {
+    return *reinterpret_cast<const bf16x8_t*>(xb + boff[st] + g * 16 * 256);
+  };
+  auto compute = [&](int slot, int next) {
     const uint8_t* xb = xbuf + slot * kXBufBytes;
     DqScale ks[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) ks[nt] = dq_scale(sc[slot][nt]);
+    bf16x8_t bwin[3];
+    bwin[0] = bread(xb, 0, 0);
+    bwin[1] = MG > 1 ? bread(xb, 0, 1) : bread(xb, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       bf16x8_t an[kNT];
-      if (st < 3) {
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) an[nt] = dequant_word(word_of(wq[slot][nt], st + 1), ks[nt]);
-      } else {
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          an[nt] = dequant_word(wq[slot ^ 1][nt].x, dq_scale(sc[slot ^ 1][nt]));
-      }
 #pragma unroll
       for (int g = 0; g < MG; ++g) {
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(xb + boff[st] + g * 16 * 256);
+        const int idx = st * MG + g;
+        const int ahead = idx + 2;
+        if (ahead < 4 * MG) bwin[ahead % 3] = bread(xb, ahead / MG, ahead % MG);
+        const bf16x8_t bv = bwin[idx % 3];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
           acc[nt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nt], bv, acc[nt][g], 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          if (nt * MG / kNT != g) continue;
+          an[nt] = st < 3 ? dequant_word(word_of(wq[slot][nt], st + 1), ks[nt])
+                          : dequant_word(wq[next][nt].x, dq_scale(sc[next][nt]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) av[nt] = an[nt];
     }
-    // Schedule: two LDS reads up front, then per token group four MFMAs each
-    // followed by a few VALU ops, then the LDS read two groups ahead.
-    constexpr int kValu = (76 + 4 * MG - 1) / (4 * MG);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * MG; ++i) {
-#pragma unroll
-      for (int m = 0; m < kNT; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-      }
-      if (i + 2 < 4 * MG) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
   };
 
-  // Chunk c in buffer `slot`: x(c+1) DMA and weights(c+1) loads into the
-  // other buffer, compute(c), barrier (which waits for this wave's DMA only).
+  // Chunk c in buffer c % 3: x(c+2) DMA and weights(c+2) loads into the
+  // buffer freed by chunk c-1, compute(c), then wait until the DMA of x(c+1)
+  // (issued one chunk ago) has landed and pass the workgroup barrier.  The
+  // barrier is a bare s_barrier with an explicit vmcnt wait: a fenced
+  // __syncthreads would also wait for the x(c+2) DMA just issued.  Loads
+  // issued after x(c+1): w(c+1) (kNT x 2), x(c+2) (MG), w(c+2) (kNT x 2).
   // Prefetch indices are clamped instead of guarded so every iteration
   // issues the same loads (exact wait counts); the clamped re-reads at the
   // end hit the caches.
+  constexpr int kWLoads = 2 * kNT;
+  constexpr int kVm = MG + 2 * kWLoads;
+  constexpr int kWaitX = (kVm & 15) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14);
   auto chunk = [&](int slot, int c) {
-    const int cn = c + 1 < nc ? c + 1 : nc - 1;
-    load_x(slot ^ 1, cn);
-    load_w(slot ^ 1, cn);
+    const int c2 = c + 2 < nc ? c + 2 : nc - 1;
+    const int fill = slot == 0 ? 2 : slot - 1;
+    load_x(fill, c2);
+    load_w(fill, c2);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-    compute(slot);
+    compute(slot, slot == 2 ? 0 : slot + 1);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitX);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  const int c1 = nc > 1 ? 1 : 0;
   load_x(0, 0);
   load_w(0, 0);
-  __syncthreads();
+  load_x(1, c1);
+  load_w(1, c1);
+  __builtin_amdgcn_s_waitcnt(kWaitX);  // x(0) landed
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) av[nt] = dequant_word(wq[0][nt].x, dq_scale(sc[0][nt]));
   int c = 0;
-  for (; c + 1 < nc; c += 2) {
+  for (; c + 2 < nc; c += 3) {
     chunk(0, c);
     chunk(1, c + 1);
+    chunk(2, c + 2);
   }
   if (c < nc) chunk(0, c);
+  if (c + 1 < nc) chunk(1, c + 1);
+  // Drain the clamped prefetches (DMA into LDS) before the buffers are
+  // reused by the next item.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
   // Epilogue: lane holds rows 4q..4q+3 of weight tile nt for token col of
   // group g.
@@ -258,8 +278,8 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
 
 __global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* xbuf = smem;                                                  // [2][192][256 B]
-  int32_t* srcoff = reinterpret_cast<int32_t*>(smem + 2 * kXBufBytes);  // [192] byte offsets
+  uint8_t* xbuf = smem;                                                  // [3][192][256 B]
+  int32_t* srcoff = reinterpret_cast<int32_t*>(smem + kStages * kXBufBytes);  // [192] byte offsets
   int64_t* dstrow = reinterpret_cast<int64_t*>(srcoff + kMaxGroups * 16);  // [192]
   const int tid = threadIdx.x;
   const int nslices = a.items_per_tile;
