@@ -48,7 +48,50 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
+                    help="instead of the layer, run `steps` plain device copies of MIB MiB "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
     return ap.parse_args()
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/traffic.json, already
+    scaled by the copy-kernel calibration), or None when there is none or the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            entries = json.load(f)["entries"]
+    except (OSError, ValueError, KeyError):
+        return None
+    for e in entries:
+        if e.get("workload") != workload or e.get("kernel") != stage:
+            continue
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), e["source"])
+        try:
+            with open(src, "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()[:16]
+        except OSError:
+            return None
+        return int(e["bytes"]) if digest == e.get("source_sha256_16") else None
+    return None
+
+
+def copy_probe(mib, steps):
+    import torch
+    n = int(mib * 2**20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes": n, "steps": steps, "read_GBs": round(n / dt / 1e9, 1)}),
+          flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -146,6 +189,9 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, args.steps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus N>1 is not supported "
                                    "(the layer takes one GPU's expert share, no collectives)"}))
@@ -252,7 +298,8 @@ def main():
         achieved = alg / (dur * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "algorithmic_bytes": int(alg), "avg_ms": round(dur, 5)}
+                "traffic": measured_traffic(spec.name, name), "algorithmic_bytes": int(alg),
+                "avg_ms": round(dur, 5)}
     else:
         name, dur, alg = "gate_up", gu_ms, work["gate_up_flops"]
         if dn_ms > gu_ms:
@@ -260,7 +307,8 @@ def main():
         achieved = alg / (dur * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(spec.name, name),
                 "algorithmic_flops": alg, "avg_ms": round(dur, 5)}
     layer_ms = sum(avg)
     extra = {"stage_ms": [round(m, 5) for m in avg], "layer_kernels_ms": round(layer_ms, 5),
