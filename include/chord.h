@@ -100,7 +100,10 @@ typedef struct {
   int32_t kernel;      /* 0 auto, 1 weight-streaming GEMMs, 2 LDS-tiled GEMMs (needs
                           I a multiple of 32, else kernel 1 runs; tiles of up to
                           192 token rows; the nt/wk/prefetch/tokens fields are
-                          then ignored) */
+                          then ignored), 3 both: experts with >= 48 rows take the
+                          tiled GEMMs (on an internal side stream, joined back
+                          to the caller's stream), the others the streaming
+                          GEMMs */
   int32_t tokens;      /* rows per token tile of kernel 1: 16 or 32; 0 auto */
   int32_t gate_up_nt;  /* 16-row weight tiles per wave in the gate_up GEMM: 2 or 4; 0 auto */
   int32_t gate_up_wk;  /* waves splitting K in the gate_up GEMM: 1, 2 or 4; 0 auto */

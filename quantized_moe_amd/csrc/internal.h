@@ -64,12 +64,20 @@ struct DevStatus {
   int32_t pad[53];
 };
 
-// Arguments of the tile builder (one workgroup).
+// Arguments of the tile builder (one workgroup).  Each expert segment goes
+// either to the small-tile list `tiles` (tiles of <= tile_tokens rows, for the
+// weight-streaming kernel; count in status->ntiles) or, when it has at least
+// split_rows rows, to the big-tile list `tiles_b` (tiles of <= big_tokens
+// rows, grouped by expert % 8, ranges in status->group_start, for the tiled
+// kernel).  split_rows = 0 sends every segment to the big list.
 struct TileBuildArgs {
   int layout;
   int num_experts;     // E_l
-  int tile_tokens;     // max rows per tile
+  int tile_tokens;     // max rows per small tile
   int max_tiles;       // capacity of `tiles`
+  int big_tokens;      // max rows per big tile
+  int max_tiles_b;     // capacity of `tiles_b`
+  int split_rows;      // segments with >= split_rows rows go to `tiles_b`
   int validate;
   // indexed
   const int32_t* expert_ids;
@@ -84,6 +92,7 @@ struct TileBuildArgs {
   int max_m;
   // out
   TileDesc* tiles;
+  TileDesc* tiles_b;
   DevStatus* status;
 };
 

@@ -94,37 +94,56 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
     }
   };
 
-  // Count tiles per expert group (expert % 8), scan each group, emit tiles
-  // group-major so that one XCD can take all tiles of its experts.
+  // Count small tiles, and big tiles per expert group (expert % 8); scan;
+  // emit small tiles in segment order and big tiles group-major so that one
+  // XCD can take all big tiles of its experts.
+  const int TOKB = a.big_tokens;
+  auto is_big = [&](int rows) { return rows >= a.split_rows; };
+  int cnt_small = 0;
   int cnt[kTileGroups];
 #pragma unroll
   for (int g = 0; g < kTileGroups; ++g) cnt[g] = 0;
-  for_each_segment([&](int e, int, int rows) { cnt[e % kTileGroups] += (rows + TOK - 1) / TOK; },
-                   true);
+  for_each_segment(
+      [&](int e, int, int rows) {
+        if (is_big(rows)) cnt[e % kTileGroups] += (rows + TOKB - 1) / TOKB;
+        else cnt_small += (rows + TOK - 1) / TOK;
+      },
+      true);
+  int total_small;
+  int base_small = block_scan_excl(cnt_small, tmp, &total_small);
   int base[kTileGroups];
   int gstart = 0;
 #pragma unroll
   for (int g = 0; g < kTileGroups; ++g) {
     int tot;
     base[g] = gstart + block_scan_excl(cnt[g], tmp, &tot);
-    if (tid == 0) a.status->group_start[g] = min(gstart, a.max_tiles);
+    if (tid == 0) a.status->group_start[g] = min(gstart, a.max_tiles_b);
     gstart += tot;
   }
-  const int total = gstart;
-  if (total > a.max_tiles && a.validate && tid == 0) atomicOr(&err, 64);
+  const int total_big = gstart;
+  if ((total_small > a.max_tiles || total_big > a.max_tiles_b) && a.validate && tid == 0)
+    atomicOr(&err, 64);
   for_each_segment(
       [&](int e, int row_begin, int rows) {
-        int& b = base[e % kTileGroups];
-        for (int r = 0; r < rows; r += TOK) {
-          if (b < a.max_tiles) a.tiles[b] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0};
-          ++b;
+        if (is_big(rows)) {
+          int& b = base[e % kTileGroups];
+          for (int r = 0; r < rows; r += TOKB) {
+            if (b < a.max_tiles_b) a.tiles_b[b] = TileDesc{e, row_begin + r, min(TOKB, rows - r), 0};
+            ++b;
+          }
+        } else {
+          for (int r = 0; r < rows; r += TOK) {
+            if (base_small < a.max_tiles)
+              a.tiles[base_small] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0};
+            ++base_small;
+          }
         }
       },
       false);
   __syncthreads();
   if (tid == 0) {
-    a.status->ntiles = min(total, a.max_tiles);
-    a.status->group_start[kTileGroups] = min(total, a.max_tiles);
+    a.status->ntiles = min(total_small, a.max_tiles);
+    a.status->group_start[kTileGroups] = min(total_big, a.max_tiles_b);
     a.status->error = err;
   }
 }

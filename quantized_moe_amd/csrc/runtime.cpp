@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -86,6 +87,8 @@ struct EnvOverrides {
   int tokens = 0;
   int gu_nt = 0, gu_wk = 0, dn_nt = 0, dn_wk = 0;  // "nt,wk" per GEMM
   int tile_wgs = 0;  // tiled kernel: workgroups per CU
+  int stream_wgs = 0;  // streaming kernel: workgroups per CU (0: balanced default)
+  int prefetch = 0;
   bool log = false;
 };
 const EnvOverrides& env() {
@@ -96,6 +99,8 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_GATE_UP")) sscanf(s, "%d,%d", &o.gu_nt, &o.gu_wk);
     if (const char* s = getenv("CHORD_W4A16_DOWN")) sscanf(s, "%d,%d", &o.dn_nt, &o.dn_wk);
     if (const char* s = getenv("CHORD_W4A16_TILE_WGS")) o.tile_wgs = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_STREAM_WGS")) o.stream_wgs = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
     return o;
   }();
@@ -128,27 +133,31 @@ struct PlanKeyHash {
   }
 };
 struct GemmPlan {
-  int kernel;  // 1 weight-streaming
-  int nt;      // 16-row weight tiles per wave
-  int wk;      // waves splitting K
-  int pf;      // K chunks in flight per wave
+  int nt;      // 16-row weight tiles per wave (streaming kernel)
+  int wk;      // waves splitting K (streaming kernel)
+  int pf;      // K chunks in flight per wave (streaming kernel)
   int grid;    // persistent workgroups
 };
+// kernel: 1 = weight-streaming GEMMs on small tiles, 2 = LDS-tiled GEMMs on
+// big tiles, 3 = both, each expert going to one of them by its row count.
 struct Plan {
-  int kernel;        // 1 weight-streaming GEMMs, 2 LDS-tiled GEMMs
-  int mt;            // 16-row token tiles per work item
-  int tile_tokens;   // rows per device tile
-  bool block_tiles;  // indexed: one tile per alignment block (no tile builder)
-  int max_tiles;
+  int kernel;
+  int mt;            // streaming kernel: 16-row token groups per tile
+  int tile_tokens;   // streaming kernel: rows per small tile
+  bool block_tiles;  // indexed: small tiles are the alignment blocks (no tile builder)
+  int max_tiles;     // small-tile list capacity
+  int max_tiles_b;   // big-tile list capacity
+  int split_rows;    // kernel 3: experts with >= split_rows rows take the tiled kernel
   int cus;
-  GemmPlan gu, dn;
-  char text[200];
+  GemmPlan gu, dn;    // streaming GEMMs
+  GemmPlan gut, dnt;  // tiled GEMMs
+  char text[240];
 };
 std::mutex g_plan_mu;
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 
 constexpr int kTileSlice = 256;    // output rows per workgroup of the tiled kernel
-constexpr int kTileTokens = 192;   // token rows per tile of the tiled kernel
+constexpr int kTileTokens = 192;   // token rows per big tile (tiled kernel)
 constexpr double kTileMinRows = 48.0;
 
 int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
@@ -156,7 +165,10 @@ int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
 }
 
 // tok_e = expected rows per local expert; the schedule follows it, not the
-// total token count.
+// total token count.  Kernel family: the LDS-tiled kernel once an expert's
+// rows amortise the in-register dequantisation over many MFMAs; the
+// weight-streaming kernel below that.  Kernel 3 (both, each expert by its row
+// count, the tiled part on a side stream) is available as an override.
 Plan make_plan(const PlanKey& key) {
   Plan p{};
   double tok_e;
@@ -169,54 +181,44 @@ Plan make_plan(const PlanKey& key) {
     tok_e = 128.0;
   }
   p.cus = key.cus;
-  // Kernel family: the LDS-tiled kernel once an expert's rows can amortise
-  // the in-register dequantisation over many MFMAs (and N fits its 256-row
-  // slices); the weight-streaming kernel below that.
   const bool tile_ok = (2 * key.I) % 64 == 0 && key.H % 64 == 0;  // 4 tiles per wave
   int kernel = key.ov[0] ? key.ov[0] : env().kernel;
-  if (kernel != 1 && kernel != 2) kernel = (tile_ok && tok_e >= kTileMinRows) ? 2 : 1;
-  if (kernel == 2 && !tile_ok) kernel = 1;
+  if (kernel < 1 || kernel > 3) kernel = tok_e >= kTileMinRows ? 2 : 1;
+  if (!tile_ok) kernel = 1;
   p.kernel = kernel;
-  if (kernel == 2) {
-    p.mt = kTileTokens / 16;
-    p.tile_tokens = kTileTokens;
-    p.block_tiles = false;
-    p.max_tiles = max_tiles_for(key.rows, key.E_l, p.tile_tokens);
-    auto tgemm = [&](int N) {
-      GemmPlan g{};
-      g.kernel = 2;
-      g.nt = 4;
-      g.wk = 1;
-      g.pf = 2;
-      const int64_t items = (int64_t)p.max_tiles * ((N + kTileSlice - 1) / kTileSlice);
-      // One workgroup per CU (registers, ~100 KB of LDS); the launcher clamps
-      // to the occupancy it measures.
-      const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 1;
-      g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
-      return g;
-    };
-    p.gu = tgemm(2 * key.I);
-    p.dn = tgemm(key.H);
-    snprintf(p.text, sizeof(p.text),
-             "tok_e=%.1f tile_tokens=%d tiles=list max_tiles=%d | gate_up tile 256x%d | down tile "
-             "256x%d",
-             tok_e, p.tile_tokens, p.max_tiles, p.tile_tokens, p.tile_tokens);
-    return p;
+  p.split_rows = kernel == 3 ? (int)kTileMinRows : (kernel == 2 ? 0 : INT32_MAX);
+  p.max_tiles_b = kernel & 2 ? max_tiles_for(key.rows, key.E_l, kTileTokens) : 0;
+
+  // Tiled GEMMs: one workgroup per CU (registers, ~150 KB of LDS); the
+  // launcher clamps to the occupancy it measures.
+  auto tgemm = [&](int N) {
+    GemmPlan g{};
+    const int64_t items = (int64_t)p.max_tiles_b * ((N + kTileSlice - 1) / kTileSlice);
+    const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 1;
+    g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
+    return g;
+  };
+  if (kernel & 2) {
+    p.gut = tgemm(2 * key.I);
+    p.dnt = tgemm(key.H);
   }
-  int mt = (int)((tok_e + 15.0) / 16.0);
+
+  // Streaming GEMMs.
+  const double tok_small = kernel == 3 ? std::min(tok_e, kTileMinRows - 1) : tok_e;
+  int mt = (int)((tok_small + 15.0) / 16.0);
   mt = std::max(1, std::min(2, mt));
   const int tokens = key.ov[1] ? key.ov[1] : env().tokens;
   if (tokens == 16 || tokens == 32) mt = tokens / 16;
   p.mt = mt;
   p.tile_tokens = mt * 16;
   // key.hint carries block_m for indexed calls.
-  p.block_tiles = key.mode == kIndexed && key.hint == p.tile_tokens;
-  p.max_tiles = p.block_tiles ? (int)((key.rows + key.hint - 1) / key.hint)
-                              : max_tiles_for(key.rows, key.E_l, p.tile_tokens);
-  const int ov_pf = key.ov[6];
+  p.block_tiles = kernel == 1 && key.mode == kIndexed && key.hint == p.tile_tokens;
+  p.max_tiles = kernel == 2 ? 0
+                : p.block_tiles ? (int)((key.rows + key.hint - 1) / key.hint)
+                                : max_tiles_for(key.rows, key.E_l, p.tile_tokens);
+  const int ov_pf = key.ov[6] ? key.ov[6] : env().prefetch;
   auto gemm = [&](int N, int K, int ov_nt, int ov_wk, int env_nt, int env_wk) {
     GemmPlan g{};
-    g.kernel = 1;
     // Defaults measured on MI355X at the decode / TP-slice shapes: deep-K
     // gate_up splits K over two waves; the short-K down GEMM runs one wave per
     // item with 4 weight tiles; very short K (<= 512) keeps 4 chunks in flight.
@@ -232,15 +234,26 @@ Plan make_plan(const PlanKey& key) {
     if ((N / 16) % g.nt != 0) g.nt = 2;
     const int64_t items = (int64_t)p.max_tiles * ((N / 16) / g.nt);
     g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)key.cus * 64));
+    if (env().stream_wgs > 0)
+      g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)key.cus * env().stream_wgs));
     return g;
   };
-  p.gu = gemm(2 * key.I, key.H, key.ov[2], key.ov[3], env().gu_nt, env().gu_wk);
-  p.dn = gemm(key.H, key.I, key.ov[4], key.ov[5], env().dn_nt, env().dn_wk);
-  snprintf(p.text, sizeof(p.text),
-           "tok_e=%.1f tile_tokens=%d tiles=%s max_tiles=%d | gate_up stream nt=%d mt=%d wk=%d "
-           "pf=%d | down stream nt=%d mt=%d wk=%d pf=%d",
-           tok_e, p.tile_tokens, p.block_tiles ? "blocks" : "list", p.max_tiles, p.gu.nt, p.mt,
-           p.gu.wk, p.gu.pf, p.dn.nt, p.mt, p.dn.wk, p.dn.pf);
+  if (kernel & 1) {
+    p.gu = gemm(2 * key.I, key.H, key.ov[2], key.ov[3], env().gu_nt, env().gu_wk);
+    p.dn = gemm(key.H, key.I, key.ov[4], key.ov[5], env().dn_nt, env().dn_wk);
+  }
+
+  const int cap = (int)sizeof(p.text);
+  int n = std::min(cap, snprintf(p.text, sizeof(p.text), "tok_e=%.1f", tok_e));
+  if (kernel & 1)
+    n += snprintf(p.text + n, sizeof(p.text) - n,
+                  " | stream tiles=%s of %d rows: gate_up nt=%d wk=%d pf=%d, down nt=%d wk=%d pf=%d",
+                  p.block_tiles ? "blocks" : "list", p.tile_tokens, p.gu.nt, p.gu.wk, p.gu.pf,
+                  p.dn.nt, p.dn.wk, p.dn.pf);
+  n = std::min(cap, n);
+  if (kernel & 2)
+    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d%s", kTileTokens,
+             kernel == 3 ? " for experts with >= 48 rows" : "");
   return p;
 }
 
@@ -300,18 +313,21 @@ struct StageTimer {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, tiles, h, y, total;
-  int max_tiles;
+  size_t status, tiles, tiles_b, h, y, total;
+  int max_tiles, max_tiles_b;
 };
 
 WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   WsLayout w{};
   w.max_tiles = max_tiles_for(rows, E_l, 16);
+  w.max_tiles_b = max_tiles_for(rows, E_l, kTileTokens);
   size_t off = 0;
   w.status = off;
   off = align_up(off + sizeof(DevStatus), 256);
   w.tiles = off;
   off = align_up(off + (size_t)w.max_tiles * sizeof(TileDesc), 256);
+  w.tiles_b = off;
+  off = align_up(off + (size_t)w.max_tiles_b * sizeof(TileDesc), 256);
   w.h = off;
   off = align_up(off + (size_t)rows * I * 2, 256);
   w.y = off;
@@ -366,16 +382,62 @@ void set_plan_text(const char* mode, const Plan& p) {
   g_last_plan = b;
 }
 
-// Launches one expert GEMM with its planned kernel.
-hipError_t launch_planned(const GemmPlan& gp, int mt, GemmArgs& g, hipStream_t stream) {
-  if (gp.kernel == 2) {
-    g.tiles_per_item = kTileSlice / kTileRows;
-    g.items_per_tile = (g.n_tiles + g.tiles_per_item - 1) / g.tiles_per_item;
-    return launch_gemm_tile(g, gp.grid, stream);
+// Side stream (one per device, default priority) on which the tiled kernel
+// runs next to the streaming kernel when both are planned (kernel 3): the
+// caller's stream forks to it and joins back through two events, so the two
+// kernels share the GPU instead of running one after the other.  Calls on one
+// device serialise on the side stream (the fork-launch-join sequence holds a
+// lock), which keeps the event reuse safe.
+struct SideStream {
+  bool ready = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t get_side(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.ready) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    ss.ready = true;
   }
-  g.tiles_per_item = gp.nt;
-  g.items_per_tile = g.n_tiles / gp.nt;
-  return launch_gemm(gp.kernel, gp.nt, mt, gp.wk, gp.pf, g, gp.grid, stream);
+  *out = &ss;
+  return hipSuccess;
+}
+
+// Launches one expert GEMM with the planned kernel(s): the streaming kernel
+// over the small-tile list, the tiled kernel over the big-tile list.
+hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* tiles_b,
+                          hipStream_t stream) {
+  GemmArgs gs = g, gt = g;
+  const GemmPlan& sp = gate_up ? plan.gu : plan.dn;
+  const GemmPlan& tp = gate_up ? plan.gut : plan.dnt;
+  gs.tiles_per_item = sp.nt;
+  gs.items_per_tile = sp.nt > 0 ? g.n_tiles / sp.nt : 0;
+  gt.tiles = tiles_b;
+  gt.tiles_per_item = kTileSlice / kTileRows;
+  gt.items_per_tile = (g.n_tiles + gt.tiles_per_item - 1) / gt.tiles_per_item;
+  gt.tile_tokens = kTileTokens;
+  if (plan.kernel == 1) return launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream);
+  if (plan.kernel == 2) return launch_gemm_tile(gt, tp.grid, stream);
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream* ss = nullptr;
+  hipError_t e;
+  if ((e = get_side(&ss)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+  if ((e = launch_gemm_tile(gt, tp.grid, ss->s)) != hipSuccess) return e;
+  if ((e = launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream)) != hipSuccess)
+    return e;
+  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+  return hipStreamWaitEvent(stream, ss->join, 0);
 }
 
 // Shared GEMM sequence: tiles -> gate_up -> down.
@@ -394,11 +456,16 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
     return fail(CHORD_ERR_UNSUPPORTED, "a layer operand exceeds 2 GiB");
   DevStatus* status = reinterpret_cast<DevStatus*>(wsp + ws.status);
   TileDesc* tiles = reinterpret_cast<TileDesc*>(wsp + ws.tiles);
+  TileDesc* tiles_b = reinterpret_cast<TileDesc*>(wsp + ws.tiles_b);
   uint16_t* h = reinterpret_cast<uint16_t*>(wsp + ws.h);
   tb.layout = layout;
   tb.tile_tokens = plan.tile_tokens;
   tb.max_tiles = std::min(plan.max_tiles, ws.max_tiles);
+  tb.big_tokens = kTileTokens;
+  tb.max_tiles_b = std::min(plan.max_tiles_b, ws.max_tiles_b);
+  tb.split_rows = plan.split_rows;
   tb.tiles = tiles;
+  tb.tiles_b = tiles_b;
   tb.status = status;
   timer.mark(0);
   if (plan.block_tiles) {
@@ -437,7 +504,7 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.out_ld = I;
   g.out_rows = rows_internal;
   g.row_weights = nullptr;
-  HIP_TRY(launch_planned(plan.gu, plan.mt, g, stream), "gate_up launch");
+  HIP_TRY(launch_planned(plan, true, g, tiles_b, stream), "gate_up launch");
   timer.mark(2);
 
   // down: B = h, out = y / out rows
@@ -452,7 +519,7 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.out_ld = H;
   g.out_rows = down_rows;
   g.row_weights = row_weights;
-  HIP_TRY(launch_planned(plan.dn, plan.mt, g, stream), "down launch");
+  HIP_TRY(launch_planned(plan, false, g, tiles_b, stream), "down launch");
   timer.mark(3);
   return CHORD_OK;
 }
@@ -681,7 +748,7 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
         if (v == o) return true;
       return false;
     };
-    if (!in(override->kernel, {0, 1, 2}) || !in(override->tokens, {0, 16, 32}) ||
+    if (!in(override->kernel, {0, 1, 2, 3}) || !in(override->tokens, {0, 16, 32}) ||
         !in(override->gate_up_nt, {0, 2, 4}) || !in(override->down_nt, {0, 2, 4}) ||
         !in(override->gate_up_wk, {0, 1, 2, 4}) || !in(override->down_wk, {0, 1, 2, 4}) ||
         !in(override->prefetch, {0, 2, 4}))

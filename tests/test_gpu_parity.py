@@ -397,3 +397,35 @@ def test_tile_kernel_masked_tile_boundaries():
     for e in range(E):
         sl = slice(e * max_m, e * max_m + mm[e])
         check_close(got[sl], ref[sl], f"masked e={e}")
+
+
+def skewed_case(seed, T, H, I, E, k, popularity):
+    """Routing with a few hot experts: each token picks k distinct experts with
+    probability proportional to `popularity`."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = G.draw_activations(rng, T, H)
+    p = np.asarray(popularity, dtype=np.float64)
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H, scale_mult=(256.0 / H) ** 0.5)
+    q2, s2 = G.draw_weights(rng, E, H, I, scale_mult=(256.0 / I) ** 0.5)
+    return x, ids, w, q13, s13, q2, s2, 0
+
+
+def test_split_kernels_indexed_bit_identical_and_oracle():
+    """Kernel 3 sends experts with >= 48 rows to the tiled kernel and the rest
+    to the streaming kernel; with one wave per K range every output keeps the
+    same accumulation order, so it must equal the streaming-only run bit for
+    bit (hot expert of ~250 rows: two big tiles)."""
+    banner("split kernels: indexed, skewed routing")
+    case = skewed_case(77, 256, 512, 256, 8, 2, [40, 20, 10, 5, 3, 2, 1, 1])
+    counts = np.bincount(case[1].ravel(), minlength=8)
+    assert counts.max() > 192 and (counts >= 48).sum() >= 2 and (counts < 48).sum() >= 2, counts
+    split, layer, _ = run_indexed(*case, E_g=8, bm=16, override={"kernel": 3})
+    assert "experts with >= 48 rows" in C.last_plan()
+    stream, _, _ = run_indexed(*case, E_g=8, bm=16, layer=layer,
+                               override={"kernel": 1, "gate_up_wk": 1, "down_wk": 1})
+    assert np.array_equal(split, stream)
+    check_close(split, oracle.moe_layer(*case))
