@@ -62,88 +62,130 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
       m = m < 0 ? 0 : (m > a.max_m ? a.max_m : m);
       first[tid] = m;  // rows
     }
+  } else {
+    // Contiguous: each expert's 128-row chunks; the segment runs from its
+    // first chunk to the last valid row of its last chunk (rows of other
+    // experts inside it, if the layout is broken, are skipped by the GEMMs'
+    // row maps).
+    const int nch = (int)(a.M / 128);
+    for (int c = tid; c < nch; c += blockDim.x) {
+      const int e = a.m_indices[(int64_t)c * 128];
+      if (e < 0 || e >= E) {
+        if (e != -1 && a.validate) atomicOr(&err, 8);
+        continue;
+      }
+      atomicMin(&first[e], c);
+      atomicMax(&last[e], c);
+      atomicAdd(&nblk[e], 1);
+      if (a.validate)
+        for (int r = 1; r < 128; ++r) {
+          const int v = a.m_indices[(int64_t)c * 128 + r];
+          if (v != e && v != -1) atomicOr(&err, (v < -1 || v >= E) ? 8 : 16);
+        }
+    }
+    __syncthreads();
+    if (tid < E && last[tid] >= 0) {
+      if (a.validate && last[tid] - first[tid] + 1 != nblk[tid]) atomicOr(&err, 16);
+      int lastv = 0;
+      for (int r = 0; r < 128; ++r)
+        if (a.m_indices[(int64_t)last[tid] * 128 + r] == tid) lastv = r + 1;
+      nblk[tid] = (last[tid] - first[tid]) * 128 + lastv;  // segment rows
+    }
   }
   __syncthreads();
 
-  // Segments owned by this thread: one expert (indexed, masked) or a range of
-  // 128-row chunks (contiguous).  f(expert, row_begin, rows).
-  const int nch = (int)(a.M / 128);
-  const int per = (nch + blockDim.x - 1) / blockDim.x;
-  auto for_each_segment = [&](auto&& f, bool check) {
+  // The segment owned by this thread: one expert.  f(expert, row_begin, rows).
+  auto for_each_segment = [&](auto&& f) {
+    if (tid >= E) return;
     if (a.layout == kIndexed) {
-      if (tid < E && last[tid] >= 0)
-        f(tid, first[tid] * a.block_m, (last[tid] - first[tid] + 1) * a.block_m);
+      if (last[tid] >= 0) f(tid, first[tid] * a.block_m, (last[tid] - first[tid] + 1) * a.block_m);
     } else if (a.layout == kMasked) {
-      if (tid < E && first[tid] > 0) f(tid, tid * a.max_m, first[tid]);
+      if (first[tid] > 0) f(tid, tid * a.max_m, first[tid]);
     } else {
-      const int c0 = tid * per, c1 = min(nch, c0 + per);
-      for (int c = c0; c < c1; ++c) {
-        const int e = a.m_indices[(int64_t)c * 128];
-        if (e < 0 || e >= E) {
-          if (check && e != -1 && a.validate) atomicOr(&err, 8);
-          continue;
-        }
-        int lastv = 0;
-        for (int r = 0; r < 128; ++r) {
-          const int v = a.m_indices[(int64_t)c * 128 + r];
-          if (v == e) lastv = r + 1;
-          else if (check && a.validate && v != -1) atomicOr(&err, (v < -1 || v >= E) ? 8 : 16);
-        }
-        f(e, c * 128, lastv);
-      }
+      if (last[tid] >= 0 && nblk[tid] > 0) f(tid, first[tid] * 128, nblk[tid]);
     }
   };
 
-  // Count small tiles, and big tiles per expert group (expert % 8); scan;
-  // emit small tiles in segment order and big tiles group-major so that one
-  // XCD can take all big tiles of its experts.
+  // Small tiles (streaming kernel) in expert order.  Big tiles (tiled
+  // kernel) are balanced over the 8 groups (one per XCD): ranked by size
+  // (rows rounded up to 32, biggest first), rank k goes to group
+  // (k / 8 even ? k % 8 : 7 - k % 8) at position k / 8 of that group.  All
+  // slices of one big tile stay in one group, so its token rows are read
+  // into one XCD's L2.
+  constexpr int kBuckets = 8;  // 32-row size classes (big tiles <= 256 rows)
   const int TOKB = a.big_tokens;
   auto is_big = [&](int rows) { return rows >= a.split_rows; };
+  auto bucket = [&](int rows) { return min(kBuckets - 1, (rows - 1) >> 5); };
   int cnt_small = 0;
-  int cnt[kTileGroups];
+  int cntb[kBuckets];
 #pragma unroll
-  for (int g = 0; g < kTileGroups; ++g) cnt[g] = 0;
-  for_each_segment(
-      [&](int e, int, int rows) {
-        if (is_big(rows)) cnt[e % kTileGroups] += (rows + TOKB - 1) / TOKB;
-        else cnt_small += (rows + TOK - 1) / TOK;
-      },
-      true);
+  for (int b = 0; b < kBuckets; ++b) cntb[b] = 0;
+  for_each_segment([&](int, int, int rows) {
+    if (is_big(rows)) {
+      for (int r = 0; r < rows; r += TOKB) ++cntb[bucket(min(TOKB, rows - r))];
+    } else {
+      cnt_small += (rows + TOK - 1) / TOK;
+    }
+  });
   int total_small;
   int base_small = block_scan_excl(cnt_small, tmp, &total_small);
-  int base[kTileGroups];
-  int gstart = 0;
-#pragma unroll
-  for (int g = 0; g < kTileGroups; ++g) {
+  int rank[kBuckets];
+  int total_big = 0;
+  for (int b = kBuckets - 1; b >= 0; --b) {  // biggest class first
     int tot;
-    base[g] = gstart + block_scan_excl(cnt[g], tmp, &tot);
-    if (tid == 0) a.status->group_start[g] = min(gstart, a.max_tiles_b);
-    gstart += tot;
+    rank[b] = total_big + block_scan_excl(cntb[b], tmp, &tot);
+    total_big += tot;
   }
-  const int total_big = gstart;
-  if ((total_small > a.max_tiles || total_big > a.max_tiles_b) && a.validate && tid == 0)
-    atomicOr(&err, 64);
-  for_each_segment(
-      [&](int e, int row_begin, int rows) {
-        if (is_big(rows)) {
-          int& b = base[e % kTileGroups];
-          for (int r = 0; r < rows; r += TOKB) {
-            if (b < a.max_tiles_b) a.tiles_b[b] = TileDesc{e, row_begin + r, min(TOKB, rows - r), 0};
-            ++b;
-          }
-        } else {
-          for (int r = 0; r < rows; r += TOK) {
-            if (base_small < a.max_tiles)
-              a.tiles[base_small] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0};
-            ++base_small;
-          }
-        }
-      },
-      false);
+  const bool big_fits = total_big <= a.max_tiles_b;
+  if ((total_small > a.max_tiles || !big_fits) && a.validate && tid == 0) atomicOr(&err, 64);
+  if (!big_fits) total_big = 0;
+  // Group g holds the ranks k with snake(k) == g: one per full round of 8,
+  // plus one if g is among the first (or, in an odd round, last) positions
+  // of the partial round.
+  const int rounds = total_big / kTileGroups, rem = total_big % kTileGroups;
+  auto group_count = [&](int g) {
+    const bool odd = rounds & 1;
+    const bool extra = odd ? g >= kTileGroups - rem : g < rem;
+    return rounds + (extra ? 1 : 0);
+  };
+  if (tid == 0) {
+    int gs = 0;
+    for (int g = 0; g < kTileGroups; ++g) {
+      a.status->group_start[g] = gs;
+      gs += group_count(g);
+    }
+    a.status->group_start[kTileGroups] = gs;
+  }
+  int gstart[kTileGroups];
+  {
+    int gs = 0;
+#pragma unroll
+    for (int g = 0; g < kTileGroups; ++g) {
+      gstart[g] = gs;
+      gs += group_count(g);
+    }
+  }
+  for_each_segment([&](int e, int row_begin, int rows) {
+    if (is_big(rows)) {
+      if (!big_fits) return;
+      for (int r = 0; r < rows; r += TOKB) {
+        const int n = min(TOKB, rows - r);
+        const int k = rank[bucket(n)]++;
+        const int pos = k % kTileGroups, rnd = k / kTileGroups;
+        const int g = (rnd & 1) ? kTileGroups - 1 - pos : pos;
+        a.tiles_b[gstart[g] + rnd] = TileDesc{e, row_begin + r, n, 0};
+      }
+    } else {
+      for (int r = 0; r < rows; r += TOK) {
+        if (base_small < a.max_tiles)
+          a.tiles[base_small] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0};
+        ++base_small;
+      }
+    }
+  });
   __syncthreads();
   if (tid == 0) {
     a.status->ntiles = min(total_small, a.max_tiles);
-    a.status->group_start[kTileGroups] = min(total_big, a.max_tiles_b);
     a.status->error = err;
   }
 }

@@ -429,3 +429,27 @@ def test_split_kernels_indexed_bit_identical_and_oracle():
                                override={"kernel": 1, "gate_up_wk": 1, "down_wk": 1})
     assert np.array_equal(split, stream)
     check_close(split, oracle.moe_layer(*case))
+
+
+def test_contiguous_validate_flags_bad_m_indices():
+    """An out-of-range m_indices value is reported with validation on; in
+    trusted mode the rows of intact segments are still computed."""
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("contiguous validate: bad m_indices")
+    x, ids, w, q13, s13, q2, s2, eb = small_case(23, 200, 256, 128, 6, 6, 2)
+    a, m_idx, f2r, nvalid = G.build_contiguous(ids, x, eb, 6)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_CONTIGUOUS)
+    good, _ = layer.contiguous(dev_bf16(a), dev(m_idx), nvalid, flags=C.FLAG_VALIDATE)
+    torch.cuda.synchronize()
+    bad = m_idx.copy()
+    seg = np.nonzero(bad == 3)[0]
+    bad[seg[0]] = 17                                   # out of range
+    with pytest.raises(C.ChordError) as ei:
+        layer.contiguous(dev_bf16(a), dev(bad), nvalid, flags=C.FLAG_VALIDATE)
+    assert ei.value.status == 5
+    rows, _ = layer.contiguous(dev_bf16(a), dev(bad), nvalid)
+    torch.cuda.synchronize()
+    keep = (bad >= 0) & (bad < 6) & (bad != 3)        # rows of intact experts
+    check_close(host_bf16(rows)[keep], host_bf16(good)[keep], "trusted rows of other experts")
+    ref = oracle.grouped_contiguous(a, m_idx, q13, s13, q2, s2)
+    check_close(host_bf16(good)[m_idx >= 0], ref[m_idx >= 0], "validated run")
