@@ -28,7 +28,7 @@ constexpr int kNT = 4;                        // weight tiles per wave
 constexpr int kMaxGroups = 12;                // 16-row token groups per tile (192 rows)
 constexpr int kXBufBytes = kMaxGroups * 16 * kChunkK * 2;  // one staged K chunk, 192 rows
 constexpr int kStages = 3;                    // token / weight buffers (two chunks in flight)
-constexpr size_t kLdsBytes = kStages * (size_t)kXBufBytes + kMaxGroups * 16 * (4 + 8);
+constexpr size_t kLdsBytes = kStages * (size_t)kXBufBytes + kMaxGroups * 16 * (4 + 8 + 4);
 
 struct DqScale {
   float s, c, s16, c16;
@@ -101,7 +101,7 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
 // each) hit 16 distinct slots: no bank conflicts.
 template <int MG>
 __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const int32_t* srcoff,
-                                         const int64_t* dstrow, int e, int ng) {
+                                         const int64_t* dstrow, const float* roww, int e, int ng) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,7 +268,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
             pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
       } else {
         const int n0 = tw * 16 + 4 * q;
-        const float rw = a.row_weights != nullptr ? a.row_weights[dr] : 1.0f;
+        const float rw = roww[g * 16 + col];
         *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
             make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
       }
@@ -281,13 +281,14 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
   uint8_t* xbuf = smem;                                                  // [3][192][256 B]
   int32_t* srcoff = reinterpret_cast<int32_t*>(smem + kStages * kXBufBytes);  // [192] byte offsets
   int64_t* dstrow = reinterpret_cast<int64_t*>(srcoff + kMaxGroups * 16);  // [192]
+  float* roww = reinterpret_cast<float*>(dstrow + kMaxGroups * 16);        // [192] row weights
   const int tid = threadIdx.x;
   const int nslices = a.items_per_tile;
 
-  // XCD-aware item order: the tile list is grouped by expert % 8; workgroup
-  // b runs on XCD b % 8 and takes the tiles of group b % 8 (all slices), so
-  // the token rows of one expert stay in that XCD's L2 across its slices.
-  // With fewer than 8 workgroups each takes several groups.
+  // XCD-aware item order: the tile list comes in 8 groups of balanced size;
+  // workgroup b runs on XCD b % 8 and takes the tiles of group b % 8 (all
+  // slices), so the token rows of one tile stay in that XCD's L2 across its
+  // slices.  With fewer than 8 workgroups each takes several groups.
   const int G = gridDim.x < kXcds ? (int)gridDim.x : kXcds;
   const int xg = blockIdx.x % G;
   const int nloc = (gridDim.x + G - 1 - xg) / G;  // workgroups serving xg
@@ -315,19 +316,247 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
         }
         srcoff[m] = so;
         dstrow[m] = dr;
+        roww[m] = (dr >= 0 && !a.gate_up && a.row_weights != nullptr) ? a.row_weights[dr] : 1.0f;
       }
       __syncthreads();
 
       // Live 16-row groups, rounded up to an even count.
       switch ((nrows + 31) >> 5) {
         case 0: break;
-        case 1: run_item<2>(a, xbuf, srcoff, dstrow, e, ng); break;
-        case 2: run_item<4>(a, xbuf, srcoff, dstrow, e, ng); break;
-        case 3: run_item<6>(a, xbuf, srcoff, dstrow, e, ng); break;
-        case 4: run_item<8>(a, xbuf, srcoff, dstrow, e, ng); break;
-        case 5: run_item<10>(a, xbuf, srcoff, dstrow, e, ng); break;
-        default: run_item<12>(a, xbuf, srcoff, dstrow, e, ng); break;
+        case 1: run_item<2>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 2: run_item<4>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 3: run_item<6>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 4: run_item<8>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 5: run_item<10>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        default: run_item<12>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
       }
+      __syncthreads();  // row maps and LDS reuse by the next item
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Short-K variant (K <= 256, e.g. the down GEMM of an 8-way intermediate
+// split): the whole token tile (all K) is staged in LDS once per work item,
+// and the item covers `slices_per_item` consecutive 256-row slices.  The
+// weights of a slice (NC chunks x 4 tiles per wave) sit in registers, double
+// buffered by slice: the next slice's weights load while this slice
+// computes.  No barrier is needed after staging.
+// ---------------------------------------------------------------------------
+template <int MG, int NC>
+__device__ __forceinline__ void run_item_shortk(const GemmArgs& a, uint8_t* xbuf,
+                                                const int32_t* srcoff, const int64_t* dstrow,
+                                                const float* roww, int e, int ng0, int ns) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4;
+  const int col = lane & 15;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Stage all NC chunks of the token tile (same DMA layout as run_item).
+  {
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
+    const int rsub = 4 * wave + q;
+    const uint32_t pbytes = (uint32_t)((col ^ rsub) * 16);
+#pragma unroll
+    for (int i = 0; i < MG; ++i) {
+      const uint32_t voff = (uint32_t)srcoff[rsub + 16 * i] + pbytes;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint8_t* dst = xbuf + c * kXBufBytes + (wave + 4 * i) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, (__attribute__((address_space(3))) void*)dst, 16, voff, c * kChunkK * 2, 0, 0);
+      }
+    }
+  }
+
+  const int64_t expert_bytes = (int64_t)a.n_tiles * NC * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+  auto tile_first = [&](int s) { return ((ng0 + s) * kWaves + wave) * kNT; };
+  uint4 wq[2][NC][kNT];
+  uint32_t sc[2][NC][kNT];
+  auto load_slice = [&](int slot, int s) {
+    int t0 = tile_first(s);
+    if (t0 > a.n_tiles - kNT) t0 = a.n_tiles - kNT;  // past the end: re-read, store nothing
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const uint32_t blk = (uint32_t)((t0 + nt) * NC + c) * kBlockBytes;
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+        wq[slot][c][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+        sc[slot][c][nt] =
+            __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+      }
+  };
+
+  f32x4_t acc[kNT][MG];
+  uint32_t boff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ col) * 16));
+
+  // One slice: NC chunks x 4 MFMA steps over MG token groups, B reads two
+  // groups ahead, the next step's dequantisation spread over the groups
+  // (the last step of the slice prepares nothing: the next slice starts by
+  // dequantising its first step).
+  auto compute_slice = [&](int slot) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int g = 0; g < MG; ++g) acc[nt][g] = zero4;
+    bf16x8_t av[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) av[nt] = dequant_word(wq[slot][0][nt].x, dq_scale(sc[slot][0][nt]));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint8_t* xb = xbuf + c * kXBufBytes;
+      DqScale ks[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) ks[nt] = dq_scale(sc[slot][c][nt]);
+      bf16x8_t bwin[3];
+      bwin[0] = *reinterpret_cast<const bf16x8_t*>(xb + boff[0]);
+      bwin[1] = *reinterpret_cast<const bf16x8_t*>(xb + (MG > 1 ? boff[0] + 16 * 256 : boff[1]));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8_t an[kNT];
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+          const int idx = st * MG + g;
+          const int ahead = idx + 2;
+          if (ahead < 4 * MG)
+            bwin[ahead % 3] = *reinterpret_cast<const bf16x8_t*>(
+                xb + boff[ahead / MG] + (ahead % MG) * 16 * 256);
+          const bf16x8_t bv = bwin[idx % 3];
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            acc[nt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nt], bv, acc[nt][g], 0, 0, 0);
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) {
+            if (nt * MG / kNT != g) continue;
+            if (st < 3) an[nt] = dequant_word(word_of(wq[slot][c][nt], st + 1), ks[nt]);
+            else if (c + 1 < NC)
+              an[nt] = dequant_word(wq[slot][c + 1][nt].x, dq_scale(sc[slot][c + 1][nt]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (st < 3 || c + 1 < NC) {
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) av[nt] = an[nt];
+        }
+      }
+    }
+  };
+
+  auto epilogue = [&](int s) {
+    const int tile0 = tile_first(s);
+    if (tile0 >= a.n_tiles) return;
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      const int64_t dr = dstrow[g * 16 + col];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        if (dr < 0) continue;
+        const f32x4_t v = acc[nt][g];
+        const int tw = tile0 + nt;
+        if (a.gate_up) {
+          const int f0 = tw * 8 + 2 * q;
+          *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
+              pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
+        } else {
+          const int n0 = tw * 16 + 4 * q;
+          const float rw = roww[g * 16 + col];
+          *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
+              make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
+        }
+      }
+    }
+  };
+
+  load_slice(0, 0);
+  __syncthreads();  // fenced: the token DMA has landed for every wave
+  // Slices in pairs so the weight buffer index is compile-time; the next
+  // slice's load is clamped to the last one (a redundant, in-bounds re-read).
+  for (int s = 0; s < ns; s += 2) {
+    load_slice(1, s + 1 < ns ? s + 1 : ns - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_slice(0);
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue(s);
+    if (s + 1 >= ns) break;
+    load_slice(0, s + 2 < ns ? s + 2 : ns - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_slice(1);
+    __builtin_amdgcn_sched_barrier(0);
+    epilogue(s + 1);
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // drain before the LDS is reused
+}
+
+__global__ __launch_bounds__(256) void gemm_tile_shortk(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* xbuf = smem;                                                  // [NC][192][256 B]
+  int32_t* srcoff = reinterpret_cast<int32_t*>(smem + kStages * kXBufBytes);
+  int64_t* dstrow = reinterpret_cast<int64_t*>(srcoff + kMaxGroups * 16);
+  float* roww = reinterpret_cast<float*>(dstrow + kMaxGroups * 16);
+  const int tid = threadIdx.x;
+  const int nslices = a.items_per_tile;
+  const int S = a.slices_per_item;
+  const int ipt = (nslices + S - 1) / S;  // items per tile
+  const int G = gridDim.x < kXcds ? (int)gridDim.x : kXcds;
+  const int xg = blockIdx.x % G;
+  const int nloc = (gridDim.x + G - 1 - xg) / G;
+  const int lidx = blockIdx.x / G;
+
+  for (int g = xg; g < kTileGroups; g += G)
+    for (int j = lidx, t0 = a.status->group_start[g],
+             n_items = (a.status->group_start[g + 1] - t0) * ipt;
+         j < n_items; j += nloc) {
+      const TileDesc td = a.tiles[t0 + j / ipt];
+      const int ng0 = (j % ipt) * S;
+      const int ns = nslices - ng0 < S ? nslices - ng0 : S;
+      const int e = td.expert;
+      const int nrows = td.nrows < kMaxGroups * 16 ? td.nrows : kMaxGroups * 16;
+      if (tid < kMaxGroups * 16) {
+        const int m = tid;
+        int32_t so = (int32_t)kNoRow;
+        int64_t dr = -1;
+        if (m < nrows) {
+          const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
+          if (rm.src >= 0) {
+            so = (int32_t)(rm.src * (int64_t)a.K * 2);
+            dr = rm.dst;
+          }
+        }
+        srcoff[m] = so;
+        dstrow[m] = dr;
+        roww[m] = (dr >= 0 && !a.gate_up && a.row_weights != nullptr) ? a.row_weights[dr] : 1.0f;
+      }
+      __syncthreads();
+#define CHORD_SHORTK(NC)                                                                   \
+  switch ((nrows + 31) >> 5) {                                                             \
+    case 0: break;                                                                         \
+    case 1: run_item_shortk<2, NC>(a, xbuf, srcoff, dstrow, roww, e, ng0, ns); break; \
+    case 2: run_item_shortk<4, NC>(a, xbuf, srcoff, dstrow, roww, e, ng0, ns); break; \
+    case 3: run_item_shortk<6, NC>(a, xbuf, srcoff, dstrow, roww, e, ng0, ns); break; \
+    case 4:                                                                                \
+      run_item_shortk<8, NC>(a, xbuf, srcoff, dstrow, roww, e, ng0, ns); \
+      break;                                                                               \
+    case 5:                                                                                \
+      run_item_shortk<10, NC>(a, xbuf, srcoff, dstrow, roww, e, ng0, ns); \
+      break;                                                                               \
+    default:                                                                               \
+      run_item_shortk<12, NC>(a, xbuf, srcoff, dstrow, roww, e, ng0, ns); \
+      break;                                                                               \
+  }
+      if (a.n_chunks == 1) {
+        CHORD_SHORTK(1)
+      } else {
+        CHORD_SHORTK(2)
+      }
+#undef CHORD_SHORTK
       __syncthreads();  // row maps and LDS reuse by the next item
     }
 }
@@ -335,6 +564,17 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream) {
+  if (a.n_chunks <= 2) {  // short K: token tile resident, several slices per item
+    static const int per_cu_s = [] {
+      hipFuncSetAttribute((const void*)gemm_tile_shortk,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+      return blocks_per_cu(gemm_tile_shortk, 256, kLdsBytes);
+    }();
+    const int cap = per_cu_s * (a.num_cus > 0 ? a.num_cus : 256);
+    hipLaunchKernelGGL(gemm_tile_shortk, dim3(grid > cap ? cap : grid), dim3(256), kLdsBytes,
+                       stream, a);
+    return hipGetLastError();
+  }
   static const int per_cu = [] {
     hipFuncSetAttribute((const void*)gemm_tile, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)kLdsBytes);

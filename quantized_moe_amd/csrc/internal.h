@@ -124,7 +124,8 @@ struct GemmArgs {
   int num_cus;           // compute units (persistent grid clamp)
   int tile_tokens;
   int tiles_per_item;    // 16-row weight tiles per work item
-  int items_per_tile;    // n_tiles / tiles_per_item
+  int items_per_tile;    // n_tiles / tiles_per_item (tiled kernel: 256-row slices)
+  int slices_per_item;   // tiled kernel, K <= 256: consecutive slices per work item
   // output
   uint16_t* out;         // h [rows, I] (gate_up) or y / out rows [*, H] (down)
   int out_ld;

@@ -223,24 +223,47 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (idx >= (int64_t)a.T * nvec) return;
   const int t = (int)(idx / nvec);
   const int v = (int)(idx % nvec);
+  // Rows through a bounds-checked buffer resource: a slot without a row gets
+  // an out-of-range offset and reads zeros, so the loads of up to 8 slots are
+  // issued together instead of one dependent branch at a time.  Products and
+  // sums keep ascending slot order.
+  const int64_t row_bytes = (int64_t)a.H * 2;
+  const int64_t span = a.n_rows * row_bytes;
+  const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.rows, 0, (int)(span < 0x7FFFFFFF ? span : 0x7FFFFFFF), 0x00020000);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; ++j) {
-    int64_t row;
-    if (a.flat_to_row != nullptr) {
-      row = a.flat_to_row[(int64_t)t * a.k + j];
-      if (row < 0 || row >= a.n_rows) continue;
-    } else {
-      const int e = a.topk_ids[(int64_t)t * a.k + j] - a.expert_begin;
-      if (e < 0 || e >= a.num_experts) continue;
-      row = (int64_t)t * a.k + j;
-    }
-    const float w = a.topk_weights[(int64_t)t * a.k + j];
-    const uint4 y = *reinterpret_cast<const uint4*>(a.rows + row * a.H + v * 8);
-    const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
+  for (int j0 = 0; j0 < a.k; j0 += 8) {
+    uint32_t off[8];
+    float wj[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += w * bf16_to_f32(yw[i] & 0xFFFFu);
-      acc[2 * i + 1] += w * bf16_to_f32(yw[i] >> 16);
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      off[u] = 0xFFFFFFFFu;
+      wj[u] = 0.f;
+      if (j >= a.k) continue;
+      int64_t row;
+      if (a.flat_to_row != nullptr) {
+        row = a.flat_to_row[(int64_t)t * a.k + j];
+        if (row < 0 || row >= a.n_rows) continue;
+      } else {
+        const int e = a.topk_ids[(int64_t)t * a.k + j] - a.expert_begin;
+        if (e < 0 || e >= a.num_experts) continue;
+        row = (int64_t)t * a.k + j;
+      }
+      off[u] = (uint32_t)(row * row_bytes + v * 16);
+      wj[u] = a.topk_weights[(int64_t)t * a.k + j];
+    }
+    u32x4_t y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = __builtin_amdgcn_raw_buffer_load_b128(rres, off[u], 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (off[u] == 0xFFFFFFFFu) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wj[u] * bf16_to_f32(y[u][i] & 0xFFFFu);
+        acc[2 * i + 1] += wj[u] * bf16_to_f32(y[u][i] >> 16);
+      }
     }
   }
   const uint4 o = make_uint4(pk_bf16(acc[0], acc[1]), pk_bf16(acc[2], acc[3]),

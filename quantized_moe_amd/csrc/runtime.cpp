@@ -133,6 +133,7 @@ struct PlanKeyHash {
   }
 };
 struct GemmPlan {
+  int slices;  // tiled kernel with K <= 256: 256-row slices per work item
   int nt;      // 16-row weight tiles per wave (streaming kernel)
   int wk;      // waves splitting K (streaming kernel)
   int pf;      // K chunks in flight per wave (streaming kernel)
@@ -191,16 +192,27 @@ Plan make_plan(const PlanKey& key) {
 
   // Tiled GEMMs: one workgroup per CU (registers, ~150 KB of LDS); the
   // launcher clamps to the occupancy it measures.
-  auto tgemm = [&](int N) {
+  // With K <= 256 the token tile stays in LDS and a work item covers several
+  // 256-row slices: as many as keep about three items per CU of expected
+  // tiles (experts x 192-row tiles each).
+  const double tiles_est = std::max(1.0, (double)key.E_l * std::ceil(std::max(tok_e, 1.0) / kTileTokens));
+  auto tgemm = [&](int N, int K) {
     GemmPlan g{};
-    const int64_t items = (int64_t)p.max_tiles_b * ((N + kTileSlice - 1) / kTileSlice);
+    const int nslices = (N + kTileSlice - 1) / kTileSlice;
+    int S = 1;
+    if (K / kChunkK <= 2) {
+      S = nslices;
+      while (S > 1 && tiles_est * ((nslices + S - 1) / S) < 3.0 * key.cus) S = (S + 1) / 2;
+    }
+    g.slices = S;
+    const int64_t items = (int64_t)p.max_tiles_b * ((nslices + S - 1) / S);
     const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 1;
     g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
     return g;
   };
   if (kernel & 2) {
-    p.gut = tgemm(2 * key.I);
-    p.dnt = tgemm(key.H);
+    p.gut = tgemm(2 * key.I, key.H);
+    p.dnt = tgemm(key.H, key.I);
   }
 
   // Streaming GEMMs.
@@ -252,7 +264,8 @@ Plan make_plan(const PlanKey& key) {
                   p.dn.nt, p.dn.wk, p.dn.pf);
   n = std::min(cap, n);
   if (kernel & 2)
-    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d%s", kTileTokens,
+    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d (slices/item %d, %d)%s",
+             kTileTokens, p.gut.slices, p.dnt.slices,
              kernel == 3 ? " for experts with >= 48 rows" : "");
   return p;
 }
@@ -425,6 +438,7 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   gt.tiles_per_item = kTileSlice / kTileRows;
   gt.items_per_tile = (g.n_tiles + gt.tiles_per_item - 1) / gt.tiles_per_item;
   gt.tile_tokens = kTileTokens;
+  gt.slices_per_item = std::max(1, std::min(tp.slices, gt.items_per_tile));
   if (plan.kernel == 1) return launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream);
   if (plan.kernel == 2) return launch_gemm_tile(gt, tp.grid, stream);
   std::lock_guard<std::mutex> lk(g_side_mu);
@@ -742,6 +756,8 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
                 (long long)max_padded);
   if ((int64_t)T * k >= ((int64_t)1 << 30) || max_padded >= ((int64_t)1 << 31))
     return fail(CHORD_ERR_UNSUPPORTED, "routing tensors too large");
+  if ((int64_t)T * k * H * 2 > INT32_MAX)  // y rows are read through a 32-bit buffer offset
+    return fail(CHORD_ERR_UNSUPPORTED, "T*k*H*2 exceeds 2 GiB");
   if (override) {
     auto in = [](int v, std::initializer_list<int> ok) {
       for (int o : ok)
@@ -812,6 +828,8 @@ chord_status chord_w4a16_moe_grouped_contiguous(
   const bool want_tokens = out_tokens != nullptr;
   if (want_tokens && (!flat_to_row || !topk_weights || T < 0 || k < 1))
     return fail(CHORD_ERR_INVALID_ARGUMENT, "token combine needs flat_to_row, topk_weights, T, k");
+  if (want_tokens && M * H * 2 > INT32_MAX)  // rows are read through a 32-bit buffer offset
+    return fail(CHORD_ERR_UNSUPPORTED, "M*H*2 exceeds 2 GiB for the token combine");
   if (M == 0) {
     if (want_tokens && T > 0) {
       CHORD_CHECK(check_device(nullptr));
