@@ -12,6 +12,8 @@
 //   * v_fma_mix_f32 computes (1024 + q) * s - 1032 * s with one rounding,
 //     which is exactly (q - 8) * s (at most 11 significant bits);
 //   * v_cvt_pk_bf16_f32 rounds two of them to bf16, nearest-even.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace chord {
@@ -135,7 +137,7 @@ template <int NT, int MT, int WK, int PF>
 __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
   extern __shared__ float red[];  // [WK][NT*MT][64][4]
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
   const int q = lane >> 4;
   const int col = lane & 15;
   const int n_items = num_tiles(a) * a.items_per_tile;
@@ -208,11 +210,23 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
           xb[p][mt][s] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
-    auto compute = [&](int p, int xp) {
+    // Chunk in weight slot p.  Once tile nt is dequantised its slot
+    // registers are free, so the load of tile nt of chunk `refill` (when
+    // do_refill)
+    // goes out right there instead of after the whole chunk: half a chunk
+    // more latency cover at no register cost.
+    auto compute = [&](int p, int xp, int refill, auto do_refill) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         bf16x8_t av[4];
         dequant_words(wq[p][nt], dq_scale(sc[p][nt]), kMaskLo, kMaskHi, kMagic, av);
+        if constexpr (decltype(do_refill)::value) {
+          const uint32_t blk = tile0 + (uint32_t)(nt * a.n_chunks + refill) * kBlockBytes;
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+          wq[p][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+          sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+          __builtin_amdgcn_sched_barrier(0);  // keep the refill where it is issued
+        }
         // No liveness branch around the MFMA: a dead token tile multiplies
         // zeros, which costs less than breaking the instruction stream.
 #pragma unroll
@@ -240,15 +254,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
           load_x((p + 1) & 1, min(c + p + 1, c_last));
-          compute(p, p & 1);
-          load_w(p, min(c + p + PF, c_last));
+          compute(p, p & 1, min(c + p + PF, c_last), std::true_type{});
         }
       }
 #pragma unroll
       for (int p = 0; p < PF - 1; ++p) {
         if (c + p < c_hi) {
           load_x((p + 1) & 1, min(c + p + 1, c_last));
-          compute(p, p & 1);
+          compute(p, p & 1, 0, std::false_type{});
         }
       }
     }

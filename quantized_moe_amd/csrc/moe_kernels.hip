@@ -223,10 +223,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (idx >= (int64_t)a.T * nvec) return;
   const int t = (int)(idx / nvec);
   const int v = (int)(idx % nvec);
-  // Rows through a bounds-checked buffer resource: a slot without a row gets
-  // an out-of-range offset and reads zeros, so the loads of up to 8 slots are
-  // issued together instead of one dependent branch at a time.  Products and
-  // sums keep ascending slot order.
+  // Rows through a buffer resource; the loads of up to 8 slots are issued
+  // together instead of one dependent branch at a time.  Products and sums
+  // keep ascending slot order.
   const int64_t row_bytes = (int64_t)a.H * 2;
   const int64_t span = a.n_rows * row_bytes;
   const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
@@ -253,9 +252,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       off[u] = (uint32_t)(row * row_bytes + v * 16);
       wj[u] = a.topk_weights[(int64_t)t * a.k + j];
     }
+    // A wave covers 512 consecutive outputs of (mostly) one token, so the
+    // guard is uniform and skips the loads of slots without a row.
     u32x4_t y[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) y[u] = __builtin_amdgcn_raw_buffer_load_b128(rres, off[u], 0, 0);
+    for (int u = 0; u < 8; ++u) {
+      y[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (off[u] != 0xFFFFFFFFu) y[u] = __builtin_amdgcn_raw_buffer_load_b128(rres, off[u], 0, 0);
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (off[u] == 0xFFFFFFFFu) continue;
