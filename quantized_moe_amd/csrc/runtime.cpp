@@ -238,6 +238,15 @@ Plan make_plan(const PlanKey& key) {
     g.nt = 4;
     g.wk = chunks >= 24 ? 2 : 1;
     g.pf = chunks <= 4 ? 4 : 2;
+    // Too few work items to cover the CUs (a handful of routed rows): narrower
+    // items (2 weight tiles) and, for deep K, a 4-way K split.
+    const double tiles_guess = std::max(1.0, std::min((double)key.E_l, key.mode == kIndexed
+                                                                          ? (double)key.T * key.k
+                                                                          : (double)key.rows));
+    if (tiles_guess * (N / 16 / 4) < key.cus) {
+      g.nt = 2;
+      if (chunks >= 16) g.wk = 4;
+    }
     const int nt = ov_nt ? ov_nt : env_nt;
     const int wk = ov_wk ? ov_wk : env_wk;
     if (nt == 2 || nt == 4) g.nt = nt;
