@@ -314,6 +314,145 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
   }
 }
 
+// Short-K variant (K <= 256, one wave per item, no K split): an item covers
+// one token tile and `slices_per_item` consecutive groups of NT weight tiles.
+// The token fragments of all K are loaded once per item; the weight loads run
+// through a four-slot ring over the item's (group, chunk) steps without a
+// break at group boundaries, each group ending with its epilogue.  Row weights
+// are read before the loop so no epilogue waits on a global load while
+// weight loads are in flight.
+template <int NT, int MT, int NC>
+__global__ __launch_bounds__(64) void gemm_stream_shortk(GemmArgs a) {
+  constexpr int PF = 4;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int col = lane & 15;
+  const int n_groups = a.n_tiles / NT;
+  const int G = a.slices_per_item;
+  const int ipt = a.items_per_tile;
+  const int n_items = num_tiles(a) * ipt;
+  const uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int ti = item / ipt;
+    const int g0 = (item % ipt) * G;
+    const TileDesc td = get_tile(a, ti);
+    const int e = td.expert;
+    if (e < 0) continue;
+    const int ng = n_groups - g0 < G ? n_groups - g0 : G;
+    const int nsteps = ng * NC;
+
+    uint32_t xoff[MT];
+    int64_t dst[MT];
+    float rw[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + col;
+      xoff[mt] = kNoRow;
+      dst[mt] = -1;
+      rw[mt] = 1.0f;
+      if (m < td.nrows) {
+        const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
+        if (rm.src >= 0) {
+          xoff[mt] = (uint32_t)((rm.src * (int64_t)a.K + q * kGroup) * 2);
+          dst[mt] = rm.dst;
+          if (!a.gate_up && a.row_weights != nullptr) rw[mt] = a.row_weights[rm.dst];
+        }
+      }
+    }
+    uint4 xb[NC][MT][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4_t v =
+              __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[mt], c * kChunkK * 2 + s * 16, 0);
+          xb[c][mt][s] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+
+    const int64_t expert_bytes = (int64_t)a.n_tiles * NC * kBlockBytes;
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+    uint4 wq[PF][NT];
+    uint32_t sc[PF][NT];
+    // Step i: group g0 + i / NC, chunk i % NC (clamped to the last step).
+    auto step_blk = [&](int i, int nt) {
+      const int ic = i < nsteps ? i : nsteps - 1;
+      const int g = g0 + ic / NC, c = ic - (ic / NC) * NC;
+      return (uint32_t)(((g * NT + nt) * NC + c) * kBlockBytes);
+    };
+    auto load_tile = [&](int slot, int i, int nt) {
+      const uint32_t blk = step_blk(i, nt);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+      wq[slot][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+      sc[slot][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+    };
+#pragma unroll
+    for (int slot = 0; slot < PF; ++slot)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) load_tile(slot, slot, nt);
+
+    f32x4_t acc[NT][MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = zero4;
+
+    auto epilogue = [&](int g) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tw = g * NT + nt;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (dst[mt] >= 0) {
+            const f32x4_t v = acc[nt][mt];
+            if (a.gate_up) {
+              const int f0 = tw * 8 + 2 * q;
+              *reinterpret_cast<uint32_t*>(a.out + dst[mt] * (int64_t)a.out_ld + f0) =
+                  pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
+            } else {
+              const int n0 = tw * 16 + 4 * q;
+              const float r = rw[mt];
+              *reinterpret_cast<uint2*>(a.out + dst[mt] * (int64_t)a.out_ld + n0) =
+                  make_uint2(pk_bf16(v[0] * r, v[1] * r), pk_bf16(v[2] * r, v[3] * r));
+            }
+          }
+          acc[nt][mt] = zero4;
+        }
+      }
+    };
+
+    for (int i0 = 0; i0 < nsteps; i0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int i = i0 + u;
+        if (i < nsteps) {
+          const int c = u % NC;  // PF is a multiple of NC
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            bf16x8_t av[4];
+            dequant_words(wq[u][nt], dq_scale(sc[u][nt]), kMaskLo, kMaskHi, kMagic, av);
+            load_tile(u, i + PF, nt);  // refill as soon as the tile is dequantised
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    av[st], as_bf16x8(xb[c][mt][st]), acc[nt][mt], 0, 0, 0);
+          }
+          if (c == NC - 1) epilogue(g0 + i / NC);
+        }
+      }
+    }
+  }
+}
+
 template <int NT, int MT, int WK, int PF>
 hipError_t launch_stream_t(const GemmArgs& a, int grid, hipStream_t stream) {
   const size_t lds = WK > 1 ? (size_t)WK * NT * MT * 64 * 4 * sizeof(float) : 0;
@@ -326,9 +465,32 @@ hipError_t launch_stream_t(const GemmArgs& a, int grid, hipStream_t stream) {
 
 }  // namespace
 
+template <int NT, int MT, int NC>
+hipError_t launch_stream_shortk_t(const GemmArgs& a, int grid, hipStream_t stream) {
+  static const int per_cu = blocks_per_cu(gemm_stream_shortk<NT, MT, NC>, 64, 0);
+  const int cap = per_cu * (a.num_cus > 0 ? a.num_cus : 256);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((gemm_stream_shortk<NT, MT, NC>), dim3(grid), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArgs& a, int grid,
                        hipStream_t stream) {
   (void)kernel;
+  if (a.slices_per_item > 0 && a.n_chunks <= 2) {  // short K: several weight-tile groups per item
+    const int key = nt * 100 + mt * 10 + a.n_chunks;
+    switch (key) {
+      case 211: return launch_stream_shortk_t<2, 1, 1>(a, grid, stream);
+      case 212: return launch_stream_shortk_t<2, 1, 2>(a, grid, stream);
+      case 221: return launch_stream_shortk_t<2, 2, 1>(a, grid, stream);
+      case 222: return launch_stream_shortk_t<2, 2, 2>(a, grid, stream);
+      case 411: return launch_stream_shortk_t<4, 1, 1>(a, grid, stream);
+      case 412: return launch_stream_shortk_t<4, 1, 2>(a, grid, stream);
+      case 421: return launch_stream_shortk_t<4, 2, 1>(a, grid, stream);
+      case 422: return launch_stream_shortk_t<4, 2, 2>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const int key = nt * 1000 + mt * 100 + wk * 10 + pf;
   switch (key) {
 #define CHORD_STREAM_CASE(NT, MT, WK, PF) \

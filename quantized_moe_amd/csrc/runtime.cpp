@@ -253,7 +253,17 @@ Plan make_plan(const PlanKey& key) {
     if (wk == 1 || wk == 2 || wk == 4) g.wk = wk;
     if (ov_pf == 2 || ov_pf == 4) g.pf = ov_pf;
     if ((N / 16) % g.nt != 0) g.nt = 2;
-    const int64_t items = (int64_t)p.max_tiles * ((N / 16) / g.nt);
+    // Short K (<= 2 chunks): an item covers several groups of weight tiles of
+    // one token tile (token fragments loaded once, weight loads pipelined
+    // across the groups), about 8 items per CU of expected tiles.
+    g.slices = 0;
+    const int n_groups = (N / 16) / g.nt;
+    if (chunks <= 2 && g.wk == 1) {
+      const double per = tiles_guess * n_groups / (8.0 * key.cus);
+      g.slices = (int)std::max(1.0, std::min((double)n_groups, std::ceil(per)));
+    }
+    const int64_t items = (int64_t)p.max_tiles *
+                          (g.slices > 0 ? (n_groups + g.slices - 1) / g.slices : n_groups);
     g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)key.cus * 64));
     if (env().stream_wgs > 0)
       g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)key.cus * env().stream_wgs));
@@ -268,9 +278,10 @@ Plan make_plan(const PlanKey& key) {
   int n = std::min(cap, snprintf(p.text, sizeof(p.text), "tok_e=%.1f", tok_e));
   if (kernel & 1)
     n += snprintf(p.text + n, sizeof(p.text) - n,
-                  " | stream tiles=%s of %d rows: gate_up nt=%d wk=%d pf=%d, down nt=%d wk=%d pf=%d",
+                  " | stream tiles=%s of %d rows: gate_up nt=%d wk=%d pf=%d, down nt=%d wk=%d pf=%d"
+                  " groups/item %d",
                   p.block_tiles ? "blocks" : "list", p.tile_tokens, p.gu.nt, p.gu.wk, p.gu.pf,
-                  p.dn.nt, p.dn.wk, p.dn.pf);
+                  p.dn.nt, p.dn.wk, p.dn.pf, p.dn.slices);
   n = std::min(cap, n);
   if (kernel & 2)
     snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d (slices/item %d, %d)%s",
@@ -443,6 +454,8 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   const GemmPlan& tp = gate_up ? plan.gut : plan.dnt;
   gs.tiles_per_item = sp.nt;
   gs.items_per_tile = sp.nt > 0 ? g.n_tiles / sp.nt : 0;
+  gs.slices_per_item = sp.slices;
+  if (sp.slices > 0) gs.items_per_tile = (gs.items_per_tile + sp.slices - 1) / sp.slices;
   gt.tiles = tiles_b;
   gt.tiles_per_item = kTileSlice / kTileRows;
   gt.items_per_tile = (g.n_tiles + gt.tiles_per_item - 1) / gt.tiles_per_item;
