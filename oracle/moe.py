@@ -349,3 +349,70 @@ def combine_rows(out_rows_bits, flat_to_row, topk_weights, H):
             if r >= 0:
                 out[t] += np.float64(topk_weights[t, j]) * y[r]
     return f64_to_bf16(out)
+
+
+# ----------------------------------------------------------------------------
+# dispatch into the grouped layouts (the step before the grouped GEMMs)
+# ----------------------------------------------------------------------------
+
+def dispatch_contiguous(x_bits, topk_ids, expert_begin, E_l, max_rows, align=128):
+    """Permute-gather of routed token rows into the contiguous grouped layout
+    ([Novita] §"Gruppierte SM90-Kernel", Abb. 3: per-expert segments padded
+    to the 128-row M-tile, ``m_indices`` marking each row's expert).  Readings:
+    segments in ascending local expert, rows in ascending flat index
+    ``t*k + j`` (the same stable order as the indexed alignment); padding rows
+    and rows past the used total carry ``m_indices = -1`` and zero data;
+    ``flat_to_row`` maps each local slot to its row and other slots to -1.
+
+    Returns ``(a [max_rows, H] bf16 bits, m_indices int32 [max_rows],
+    flat_to_row int32 [T*k], num_rows)``.
+    """
+    T, k = topk_ids.shape
+    H = x_bits.shape[1]
+    flat = topk_ids.reshape(-1).astype(np.int64) - expert_begin
+    a = np.zeros((max_rows, H), dtype=np.uint16)
+    m_indices = np.full(max_rows, -1, dtype=np.int32)
+    flat_to_row = np.full(T * k, -1, dtype=np.int32)
+    row = 0
+    for e in range(E_l):
+        members = [i for i in range(T * k) if flat[i] == e]
+        if not members:
+            continue
+        for r, i in enumerate(members):
+            m_indices[row + r] = e
+            flat_to_row[i] = row + r
+            a[row + r] = x_bits[i // k]
+        row += ((len(members) + align - 1) // align) * align
+    assert row <= max_rows, "buffer smaller than the padded total"
+    return a, m_indices, flat_to_row, row
+
+
+def dispatch_masked(x_bits, topk_ids, expert_begin, E_l, max_m):
+    """Permute-gather into the masked grouped layout ([Novita]
+    §"Gruppierte SM90-Kernel": a fixed ``[E, max_m, H]`` buffer with the valid
+    row count ``masked_m[e]`` per expert).  Readings: rows of an expert keep
+    ascending flat index; an expert with more than ``max_m`` slots keeps the
+    first ``max_m`` and the others are dropped (their ``flat_to_row`` is -1, so
+    a combine treats them like non-local slots) and counted; rows past
+    ``masked_m[e]`` are left zero.
+
+    Returns ``(a3 [E_l, max_m, H] bf16 bits, masked_m int32 [E_l],
+    flat_to_row int32 [T*k] (row e*max_m + r, or -1), dropped)``.
+    """
+    T, k = topk_ids.shape
+    H = x_bits.shape[1]
+    flat = topk_ids.reshape(-1).astype(np.int64) - expert_begin
+    a3 = np.zeros((E_l, max_m, H), dtype=np.uint16)
+    masked_m = np.zeros(E_l, dtype=np.int32)
+    flat_to_row = np.full(T * k, -1, dtype=np.int32)
+    dropped = 0
+    for e in range(E_l):
+        members = [i for i in range(T * k) if flat[i] == e]
+        for r, i in enumerate(members):
+            if r < max_m:
+                a3[e, r] = x_bits[i // k]
+                flat_to_row[i] = e * max_m + r
+            else:
+                dropped += 1
+        masked_m[e] = min(len(members), max_m)
+    return a3, masked_m, flat_to_row, dropped

@@ -513,3 +513,82 @@ def test_planted_mistakes_fail_pins(monkeypatch, mutation):
         monkeypatch.setattr(om, "combine", bad)
     got = om.bf16_to_f64(om.moe_layer(*args))
     assert not np.array_equal(got, exp)
+
+
+# ----------------------------------------------------------------------------
+# dispatch into the grouped layouts
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,E_g,E_l,eb", [(30, 4, 16, 6, 3), (7, 8, 8, 8, 0), (50, 2, 64, 5, 60)])
+def test_dispatch_contiguous_against_generator_and_invariants(T, k, E_g, E_l, eb):
+    """Pinned against the input generator's independent builder, plus the
+    layout's invariants (every local slot once, 128-row segments of one
+    expert in ascending order, gathered rows equal the token rows)."""
+    rng = np.random.default_rng(T * 100 + E_l)
+    x = G.draw_activations(rng, T, 32)
+    ids, _ = G.draw_routing(rng, T, E_g, k)
+    a_g, m_g, f_g, _ = G.build_contiguous(ids, x, eb, E_l)
+    M = a_g.shape[0]
+    a, m, f, rows = om.dispatch_contiguous(x, ids, eb, E_l, M + 256)
+    assert rows == M
+    assert np.array_equal(a[:M], a_g) and np.array_equal(m[:M], m_g) and np.array_equal(f, f_g)
+    assert (m[M:] == -1).all() and (a[M:] == 0).all()
+    flat = ids.reshape(-1) - eb
+    local = (flat >= 0) & (flat < E_l)
+    assert sorted(f[local].tolist()) == sorted(set(f[local].tolist()))          # one row per slot
+    assert (f[~local] == -1).all()
+    for i in np.nonzero(local)[0]:
+        assert m[f[i]] == flat[i] and np.array_equal(a[f[i]], x[i // k])
+    for c in range(M // 128):                                                   # one expert per chunk
+        vals = set(m[c * 128:(c + 1) * 128].tolist()) - {-1}
+        assert len(vals) <= 1
+    assert (np.diff(m[m >= 0]) >= 0).all()                                      # ascending experts
+
+
+@pytest.mark.parametrize("max_m", [64, 3])
+def test_dispatch_masked_brute_force(max_m):
+    """Brute force over the slots: rank of a slot among its expert's slots in
+    flat order decides its row; ranks >= max_m are dropped and counted."""
+    rng = np.random.default_rng(5 + max_m)
+    T, k, E_g, E_l, eb = 40, 4, 12, 5, 2
+    x = G.draw_activations(rng, T, 16)
+    ids, _ = G.draw_routing(rng, T, E_g, k)
+    a3, mm, f, dropped = om.dispatch_masked(x, ids, eb, E_l, max_m)
+    flat = (ids.reshape(-1) - eb).tolist()
+    seen = [0] * E_l
+    exp_drop = 0
+    for i, e in enumerate(flat):
+        if not 0 <= e < E_l:
+            assert f[i] == -1
+            continue
+        r = seen[e]
+        seen[e] += 1
+        if r < max_m:
+            assert f[i] == e * max_m + r and np.array_equal(a3[e, r], x[i // k])
+        else:
+            assert f[i] == -1
+            exp_drop += 1
+    assert dropped == exp_drop and mm.tolist() == [min(c, max_m) for c in seen]
+    for e in range(E_l):
+        assert (a3[e, mm[e]:] == 0).all()
+    if max_m == 3:
+        assert dropped > 0
+
+
+def test_dispatch_then_grouped_layers_equal_the_definition():
+    """Dispatch + grouped layer + row combine reproduce the layer exactly
+    (fp64 oracle arithmetic in both; the grouped rows are bf16, so the
+    reference combines bf16-rounded y) when nothing is dropped."""
+    x, ids, w, q13, s13, q2, s2, eb = tiny_workload(11)
+    T, k = ids.shape
+    E_l = q13.shape[0]
+    ys = om.routed_y(x, ids, q13, s13, q2, s2, eb)
+    ys = {tj: om.bf16_to_f64(om.f64_to_bf16(y)) for tj, y in ys.items()}
+    ref = om.combine(ys, ids, w, eb, E_l, x.shape[1], np.arange(T))
+    a, m, f, rows = om.dispatch_contiguous(x, ids, eb, E_l, T * k + E_l * 128)
+    yc = om.grouped_contiguous(a, m, q13, s13, q2, s2)
+    assert np.array_equal(om.combine_rows(yc, f, w, x.shape[1]), ref)
+    a3, mm, f3, dropped = om.dispatch_masked(x, ids, eb, E_l, T * k)
+    assert dropped == 0
+    ym = om.grouped_masked(a3, mm, q13, s13, q2, s2)
+    assert np.array_equal(om.combine_rows(ym, f3, w, x.shape[1]), ref)
