@@ -207,6 +207,90 @@ chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_b
                              void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Dispatch into the grouped layouts, and the combine back to tokens
+ * ([Novita] §"Gruppierte SM90-Kernel" and Abb. 3: the grouped kernels take
+ * activations already permuted per expert; [aihirek] §"Ket kulon
+ * kernelcsalad").  Rows keep the alignment's stable order: ascending local
+ * expert, ascending flat slot id i = t*k + j inside an expert.
+ * ------------------------------------------------------------------------- */
+
+/* Rows the contiguous dispatch needs: T*k + E_l*127 rounded up to 128. */
+int64_t chord_moe_dispatch_contiguous_rows(int T, int k, int num_local_experts);
+
+/* Workspace bytes of chord_moe_dispatch_contiguous (mode
+ * CHORD_MODE_CONTIGUOUS) or chord_moe_dispatch_masked (CHORD_MODE_MASKED);
+ * 0 for bad arguments. */
+size_t chord_moe_dispatch_workspace_bytes(int mode, int T, int k, int num_local_experts);
+
+/*
+ * Permute-gather into the contiguous grouped layout: each local expert's
+ * slots become a segment of rows padded to a multiple of 128 (the GEMM's
+ * M-tile), segments in ascending expert order.
+ *
+ * x:          device bf16 [T, H], 16-byte aligned; H % 8 == 0.
+ * topk_ids:   device int32 [T, k], global expert ids; local ones lie in
+ *             [expert_begin, expert_begin + num_local_experts).
+ * a:          device bf16 [max_rows, H] out, 16-byte aligned.  Rows below
+ *             *num_rows hold x[t] of their slot, padding rows are 0; rows from
+ *             *num_rows on are not written.
+ * m_indices:  device int32 [max_rows] out: local expert of each row, -1 for
+ *             padding and for every row from *num_rows on.
+ * max_rows:   multiple of 128, >= chord_moe_dispatch_contiguous_rows(T, k,
+ *             E_l) (a bound that holds for any routing, so the call needs no
+ *             host readback).
+ * flat_to_row: device int32 [T*k] out: row of each local slot, -1 for the
+ *             others (the combine contract of chord_w4a16_moe_grouped_contiguous
+ *             and chord_moe_combine).
+ * num_rows:   device int32 [1] out: rows used, a multiple of 128.
+ * workspace:  device, chord_moe_dispatch_workspace_bytes(CHORD_MODE_CONTIGUOUS,
+ *             ...) bytes, caller-owned; holds the alignment between calls.
+ * Enqueued on `stream`; outputs are deterministic.
+ */
+chord_status chord_moe_dispatch_contiguous(const chord_bf16* x, int T, int H,
+                                           const int32_t* topk_ids, int k, int expert_begin,
+                                           int num_local_experts, chord_bf16* a,
+                                           int32_t* m_indices, int64_t max_rows,
+                                           int32_t* flat_to_row, int32_t* num_rows,
+                                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Permute-gather into the masked grouped layout: slot number r (in the stable
+ * order) of local expert e goes to a3[e, r] while r < max_m; later slots of a
+ * hot expert are dropped, counted, and map to no row.
+ *
+ * x, topk_ids, H, expert_begin: as for the contiguous dispatch.
+ * a3:         device bf16 [num_local_experts, max_m, H] out, 16-byte aligned;
+ *             rows from masked_m[e] on are not written.
+ * masked_m:   device int32 [num_local_experts] out: min(slots of e, max_m).
+ * flat_to_row: device int32 [T*k] out: e*max_m + r for a kept slot, -1 for a
+ *             dropped or non-local one.
+ * dropped:    device int32 [1] out: slots dropped over all experts.
+ * workspace:  chord_moe_dispatch_workspace_bytes(CHORD_MODE_MASKED, ...) bytes.
+ * max_m >= 1; num_local_experts * max_m < 2^31.  Enqueued on `stream`.
+ */
+chord_status chord_moe_dispatch_masked(const chord_bf16* x, int T, int H, const int32_t* topk_ids,
+                                       int k, int expert_begin, int num_local_experts, int max_m,
+                                       chord_bf16* a3, int32_t* masked_m, int32_t* flat_to_row,
+                                       int32_t* dropped, void* workspace, size_t ws_bytes,
+                                       void* stream);
+
+/*
+ * Unpermute-combine: out[t] = bf16( sum over j with flat_to_row[t*k+j] in
+ * [0, n_rows) of topk_weights[t,j] * rows[flat_to_row[t*k+j]] ), fp32
+ * accumulation in ascending j: the weighted top-k sum that ends the MoE
+ * layer, for the grouped layouts whose GEMMs stop at per-row outputs
+ * ([Novita] §"Gruppierte SM90-Kernel").  Tokens with no such slot get 0.
+ *
+ * rows:       device bf16 [n_rows, H] (e.g. the masked layer's flat output),
+ *             16-byte aligned; n_rows * H * 2 < 2^31.
+ * flat_to_row: device int32 [T*k]; topk_weights: device fp32 [T, k].
+ * out:        device bf16 [T, H], every row written.  Enqueued on `stream`.
+ */
+chord_status chord_moe_combine(const chord_bf16* rows, int64_t n_rows, int H,
+                               const int32_t* flat_to_row, const float* topk_weights, int T,
+                               int k, chord_bf16* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * The layer
  * ------------------------------------------------------------------------- */
 

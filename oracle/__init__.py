@@ -24,4 +24,6 @@ from .moe import (  # noqa: F401
     grouped_contiguous,
     grouped_masked,
     combine_rows,
+    dispatch_contiguous,
+    dispatch_masked,
 )

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libchord.so")
 SOURCES = ["runtime.cpp", "align.hip", "pack.hip", "moe_kernels.hip", "gemm_stream.hip",
-           "gemm_tile.hip"]
+           "gemm_tile.hip", "dispatch.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

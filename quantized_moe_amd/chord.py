@@ -30,6 +30,8 @@ EXPORTED = [
     "chord_moe_align_workspace_bytes", "chord_moe_align", "chord_w4a16_moe_indexed_block_m",
     "chord_w4a16_moe_workspace_bytes", "chord_w4a16_moe_indexed",
     "chord_w4a16_moe_grouped_contiguous", "chord_w4a16_moe_grouped_masked",
+    "chord_moe_dispatch_contiguous_rows", "chord_moe_dispatch_workspace_bytes",
+    "chord_moe_dispatch_contiguous", "chord_moe_dispatch_masked", "chord_moe_combine",
 ]
 
 
@@ -81,6 +83,11 @@ def _load():
                                                    P, SZ, ctypes.POINTER(Schedule), U32, P]),
         "chord_w4a16_moe_grouped_masked": (I, [P, I, I, P, I, WP, WP, I, I, P, P, P, SZ,
                                                ctypes.POINTER(Schedule), U32, P]),
+        "chord_moe_dispatch_contiguous_rows": (I64, [I, I, I]),
+        "chord_moe_dispatch_workspace_bytes": (SZ, [I, I, I, I]),
+        "chord_moe_dispatch_contiguous": (I, [P, I, I, P, I, I, I, P, P, I64, P, P, P, SZ, P]),
+        "chord_moe_dispatch_masked": (I, [P, I, I, P, I, I, I, I, P, P, P, P, P, SZ, P]),
+        "chord_moe_combine": (I, [P, I64, I, P, P, I, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -266,4 +273,72 @@ def chord_w4a16_moe_grouped_masked(a3, masked_m, expected_m, w13: PackedWeight, 
         _ptr(a3), E, max_m, _ptr(masked_m), expected_m, ctypes.byref(w13.handle),
         ctypes.byref(w2.handle), H, I, _ptr(row_weights), _ptr(out), _ptr(workspace),
         workspace.numel(), _sched(override), flags, _stream(stream)))
+    return out
+
+
+def chord_moe_dispatch_contiguous_rows(T: int, k: int, E_l: int) -> int:
+    return lib.chord_moe_dispatch_contiguous_rows(T, k, E_l)
+
+
+def chord_moe_dispatch_workspace_bytes(mode: int, T: int, k: int, E_l: int) -> int:
+    return lib.chord_moe_dispatch_workspace_bytes(mode, T, k, E_l)
+
+
+def chord_moe_dispatch_contiguous(x, topk_ids, expert_begin: int, num_local_experts: int,
+                                  max_rows: Optional[int] = None, out=None, workspace=None,
+                                  stream=None):
+    """Returns (a [max_rows, H], m_indices [max_rows], flat_to_row [T*k], num_rows [1])."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    if max_rows is None:
+        max_rows = lib.chord_moe_dispatch_contiguous_rows(T, k, num_local_experts)
+    if out is None:
+        a = torch.empty((max_rows, H), dtype=torch.bfloat16, device=dev)
+        m_indices = torch.empty(max_rows, dtype=torch.int32, device=dev)
+        flat_to_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+        num_rows = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        a, m_indices, flat_to_row, num_rows = out
+    if workspace is None:
+        ws = lib.chord_moe_dispatch_workspace_bytes(MODE_CONTIGUOUS, T, k, num_local_experts)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(lib.chord_moe_dispatch_contiguous(
+        _ptr(x), T, H, _ptr(topk_ids), k, expert_begin, num_local_experts, _ptr(a),
+        _ptr(m_indices), max_rows, _ptr(flat_to_row), _ptr(num_rows), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return a, m_indices, flat_to_row, num_rows
+
+
+def chord_moe_dispatch_masked(x, topk_ids, expert_begin: int, num_local_experts: int, max_m: int,
+                              out=None, workspace=None, stream=None):
+    """Returns (a3 [E_l, max_m, H], masked_m [E_l], flat_to_row [T*k], dropped [1])."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    if out is None:
+        a3 = torch.empty((num_local_experts, max_m, H), dtype=torch.bfloat16, device=dev)
+        masked_m = torch.empty(num_local_experts, dtype=torch.int32, device=dev)
+        flat_to_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+        dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        a3, masked_m, flat_to_row, dropped = out
+    if workspace is None:
+        ws = lib.chord_moe_dispatch_workspace_bytes(MODE_MASKED, T, k, num_local_experts)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(lib.chord_moe_dispatch_masked(
+        _ptr(x), T, H, _ptr(topk_ids), k, expert_begin, num_local_experts, max_m, _ptr(a3),
+        _ptr(masked_m), _ptr(flat_to_row), _ptr(dropped), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return a3, masked_m, flat_to_row, dropped
+
+
+def chord_moe_combine(rows, flat_to_row, topk_weights, out=None, stream=None):
+    """out[t] = bf16(sum_j topk_weights[t,j] * rows[flat_to_row[t*k+j]]) over slots with a row."""
+    n_rows, H = rows.shape
+    T, k = topk_weights.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=rows.device)
+    _check(lib.chord_moe_combine(_ptr(rows), n_rows, H, _ptr(flat_to_row), _ptr(topk_weights), T, k,
+                                 _ptr(out), _stream(stream)))
     return out

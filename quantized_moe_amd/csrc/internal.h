@@ -158,6 +158,28 @@ struct AlignArgs {
   int nchunks;
 };
 
+// Arguments of the dispatch gathers (grouped layouts built from an
+// alignment: sorted_ids / expert_ids / ntpp with block_m-row blocks).
+struct DispatchArgs {
+  const uint16_t* x;          // token rows [T, H] bf16
+  const int32_t* topk_ids;    // [T, k] global expert ids
+  int T, k, H;
+  int expert_begin, num_experts;
+  const int32_t* sorted_ids;  // alignment
+  const int32_t* expert_ids;
+  const int32_t* ntpp;
+  int block_m;
+  int64_t max_padded;
+  uint16_t* out;              // contiguous a [max_rows, H] / masked a3 [E, max_m, H]
+  int64_t max_rows;           // contiguous
+  int32_t* m_indices;         // contiguous [max_rows]
+  int32_t* num_rows;          // contiguous [1]
+  int max_m;                  // masked
+  int32_t* masked_m;          // masked [E]
+  int32_t* dropped;           // masked [1]
+  int32_t* flat_to_row;       // [T * k]
+};
+
 // Launchers (defined in the .hip files).  All enqueue on `stream` and return
 // hipSuccess or the launch error.
 hipError_t launch_pack(const int32_t* q, const uint16_t* s, int E, int N, int K, int gate_up,
@@ -175,6 +197,8 @@ hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArg
 // 4 weight tiles per wave, 256 output rows per workgroup; N a multiple of 64).
 hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_gather_contiguous(const DispatchArgs& a, hipStream_t stream);
+hipError_t launch_gather_masked(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream);
 
 constexpr int kAlignChunk = 8192;       // entries per align workgroup

@@ -572,6 +572,81 @@ chord_status finish_validate(uint32_t flags, const WsLayout& ws, uint8_t* wsp, h
 
 }  // namespace
 
+// Dispatch into the grouped layouts: shared checks, workspace layout and the
+// alignment step both layouts start from.
+namespace {
+
+constexpr int kContigBlock = 128;  // contiguous segments pad to the M-tile
+constexpr int kMaskedBlock = 16;   // masked dispatch: smallest alignment block
+
+struct DispatchWs {
+  size_t align_off, sorted_off, experts_off, ntpp_off, total;
+  int64_t max_padded;
+};
+
+DispatchWs dispatch_ws(int T, int k, int E_l, int block_m) {
+  DispatchWs w{};
+  w.max_padded = chord_moe_align_max_padded(T, k, E_l, block_m);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  w.align_off = take(chord_moe_align_workspace_bytes(T, k, E_l, block_m));
+  w.sorted_off = take((size_t)w.max_padded * sizeof(int32_t));
+  w.experts_off = take((size_t)((w.max_padded + block_m - 1) / block_m) * sizeof(int32_t));
+  w.ntpp_off = take(sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+// Shared argument checks and the alignment step of both dispatch layouts.
+chord_status dispatch_prepare(const chord_bf16* x, int T, int H, const int32_t* topk_ids, int k,
+                              int expert_begin, int E_l, int block_m, int32_t* flat_to_row,
+                              void* workspace, size_t ws_bytes, hipStream_t st, DispatchArgs* d) {
+  if (T < 0 || k < 1 || H <= 0) return fail(CHORD_ERR_INVALID_ARGUMENT, "T=%d k=%d H=%d", T, k, H);
+  if (H % 8 != 0) return fail(CHORD_ERR_UNSUPPORTED, "H=%d must be a multiple of 8", H);
+  if (E_l < 1 || E_l > kMaxExperts)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "num_local_experts=%d (1..%d)", E_l, kMaxExperts);
+  if ((int64_t)T * k >= ((int64_t)1 << 30)) return fail(CHORD_ERR_UNSUPPORTED, "T*k too large");
+  if (T > 0 && (!x || !topk_ids || !flat_to_row))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(x) % 16 != 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned");
+  const DispatchWs w = dispatch_ws(T, k, E_l, block_m);
+  if (!workspace || ws_bytes < w.total)
+    return fail(CHORD_ERR_WORKSPACE, "dispatch workspace %zu bytes, %zu needed", ws_bytes,
+                w.total);
+  // Host checks are done; chord_moe_align checks the device before launching.
+  uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(wsp + w.sorted_off);
+  int32_t* experts = reinterpret_cast<int32_t*>(wsp + w.experts_off);
+  int32_t* ntpp = reinterpret_cast<int32_t*>(wsp + w.ntpp_off);
+  const chord_status s =
+      chord_moe_align(topk_ids, T, k, expert_begin, E_l, block_m, sorted, experts, ntpp,
+                      w.max_padded, wsp + w.align_off,
+                      chord_moe_align_workspace_bytes(T, k, E_l, block_m), 0, st);
+  if (s != CHORD_OK) return s;
+  *d = DispatchArgs{};
+  d->x = reinterpret_cast<const uint16_t*>(x);
+  d->topk_ids = topk_ids;
+  d->T = T;
+  d->k = k;
+  d->H = H;
+  d->expert_begin = expert_begin;
+  d->num_experts = E_l;
+  d->sorted_ids = sorted;
+  d->expert_ids = experts;
+  d->ntpp = ntpp;
+  d->block_m = block_m;
+  d->max_padded = w.max_padded;
+  d->flat_to_row = flat_to_row;
+  return CHORD_OK;
+}
+
+}  // namespace
+
 // ===========================================================================
 // Public C ABI
 // ===========================================================================
@@ -736,6 +811,107 @@ chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_b
   const hipError_t e = launch_align(a, static_cast<hipStream_t>(stream));
   HIP_TRY(e, "align launch");
   g_last_plan = single ? "align: single workgroup" : "align: count/offsets/scatter";
+  return CHORD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch into the grouped layouts and the standalone combine.
+// ---------------------------------------------------------------------------
+
+int64_t chord_moe_dispatch_contiguous_rows(int T, int k, int num_local_experts) {
+  const int64_t b = chord_moe_align_max_padded(T, k, num_local_experts, kContigBlock);
+  if (b <= 0) return 0;
+  return (b + kContigBlock - 1) / kContigBlock * kContigBlock;
+}
+
+size_t chord_moe_dispatch_workspace_bytes(int mode, int T, int k, int num_local_experts) {
+  if (T < 0 || k < 1 || num_local_experts < 1) return 0;
+  if (mode == CHORD_MODE_CONTIGUOUS) return dispatch_ws(T, k, num_local_experts, kContigBlock).total;
+  if (mode == CHORD_MODE_MASKED) return dispatch_ws(T, k, num_local_experts, kMaskedBlock).total;
+  return 0;
+}
+
+chord_status chord_moe_dispatch_contiguous(const chord_bf16* x, int T, int H,
+                                           const int32_t* topk_ids, int k, int expert_begin,
+                                           int num_local_experts, chord_bf16* a,
+                                           int32_t* m_indices, int64_t max_rows,
+                                           int32_t* flat_to_row, int32_t* num_rows,
+                                           void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!a || !m_indices || !num_rows) return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(a) % 16 != 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "a must be 16-byte aligned");
+  const int64_t need = chord_moe_dispatch_contiguous_rows(T, k, num_local_experts);
+  if (max_rows < need || max_rows % kContigBlock != 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT,
+                "max_rows=%lld: needs a multiple of 128 of at least %lld", (long long)max_rows,
+                (long long)need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DispatchArgs d{};
+  CHORD_CHECK(dispatch_prepare(x, T, H, topk_ids, k, expert_begin, num_local_experts,
+                               kContigBlock, flat_to_row, workspace, ws_bytes, st, &d));
+  d.out = reinterpret_cast<uint16_t*>(a);
+  d.max_rows = max_rows;
+  d.m_indices = m_indices;
+  d.num_rows = num_rows;
+  HIP_TRY(launch_gather_contiguous(d, st), "dispatch launch");
+  g_last_plan = "dispatch: align (128-row blocks) + contiguous gather";
+  return CHORD_OK;
+}
+
+chord_status chord_moe_dispatch_masked(const chord_bf16* x, int T, int H, const int32_t* topk_ids,
+                                       int k, int expert_begin, int num_local_experts, int max_m,
+                                       chord_bf16* a3, int32_t* masked_m, int32_t* flat_to_row,
+                                       int32_t* dropped, void* workspace, size_t ws_bytes,
+                                       void* stream) {
+  g_last_error.clear();
+  if (max_m < 1) return fail(CHORD_ERR_INVALID_ARGUMENT, "max_m=%d must be positive", max_m);
+  if (!a3 || !masked_m || !dropped) return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(a3) % 16 != 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "a3 must be 16-byte aligned");
+  if ((int64_t)num_local_experts * max_m >= ((int64_t)1 << 31))
+    return fail(CHORD_ERR_UNSUPPORTED, "E*max_m too large");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DispatchArgs d{};
+  CHORD_CHECK(dispatch_prepare(x, T, H, topk_ids, k, expert_begin, num_local_experts,
+                               kMaskedBlock, flat_to_row, workspace, ws_bytes, st, &d));
+  d.out = reinterpret_cast<uint16_t*>(a3);
+  d.max_m = max_m;
+  d.masked_m = masked_m;
+  d.dropped = dropped;
+  HIP_TRY(launch_gather_masked(d, st), "dispatch launch");
+  g_last_plan = "dispatch: align (16-row blocks) + masked gather";
+  return CHORD_OK;
+}
+
+chord_status chord_moe_combine(const chord_bf16* rows, int64_t n_rows, int H,
+                               const int32_t* flat_to_row, const float* topk_weights, int T,
+                               int k, chord_bf16* out, void* stream) {
+  g_last_error.clear();
+  if (T < 0 || k < 1 || H <= 0 || n_rows < 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "T=%d k=%d H=%d n_rows=%lld", T, k, H,
+                (long long)n_rows);
+  if (H % 8 != 0) return fail(CHORD_ERR_UNSUPPORTED, "H=%d must be a multiple of 8", H);
+  if (T == 0) return CHORD_OK;
+  if (!flat_to_row || !topk_weights || !out || (n_rows > 0 && !rows))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(rows) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "rows and out must be 16-byte aligned");
+  if (n_rows * H * 2 > INT32_MAX)
+    return fail(CHORD_ERR_UNSUPPORTED, "rows span more than 2 GiB");
+  CHORD_CHECK(check_device(nullptr));
+  CombineArgs c{};
+  c.rows = reinterpret_cast<const uint16_t*>(rows);
+  c.topk_ids = nullptr;
+  c.flat_to_row = flat_to_row;
+  c.topk_weights = topk_weights;
+  c.T = T;
+  c.k = k;
+  c.H = H;
+  c.n_rows = n_rows;
+  c.out = reinterpret_cast<uint16_t*>(out);
+  HIP_TRY(launch_combine(c, static_cast<hipStream_t>(stream)), "combine launch");
+  g_last_plan = "combine";
   return CHORD_OK;
 }
 

@@ -137,3 +137,36 @@ def test_product_path_never_imports_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", txt, re.M), f
                 assert "oracle/" not in txt, f
+
+
+def test_dispatch_and_combine_host_validation():
+    L = C.lib
+    assert C.chord_moe_dispatch_contiguous_rows(64, 8, 48) == (512 + 48 * 127 + 127) // 128 * 128
+    ws_c = C.chord_moe_dispatch_workspace_bytes(C.MODE_CONTIGUOUS, 64, 8, 48)
+    ws_m = C.chord_moe_dispatch_workspace_bytes(C.MODE_MASKED, 64, 8, 48)
+    assert ws_c > 0 and ws_m > 0
+    assert C.chord_moe_dispatch_workspace_bytes(C.MODE_INDEXED, 64, 8, 48) == 0
+    rows = C.chord_moe_dispatch_contiguous_rows(4, 2, 8)
+
+    def contig(H=256, max_rows=rows, ws=1 << 20, x=FAKE, E=8):
+        return L.chord_moe_dispatch_contiguous(x, 4, H, FAKE, 2, 0, E, FAKE, FAKE, max_rows, FAKE,
+                                               FAKE, FAKE, ws, None)
+
+    assert contig(max_rows=rows - 128) == 1                 # below the routing-independent bound
+    assert contig(max_rows=rows + 1) == 1                   # not a multiple of 128
+    assert contig(H=100) == 2                               # H % 8
+    assert contig(ws=16) == 4
+    assert contig(x=ctypes.c_void_p(0x1008)) == 1           # misaligned rows
+    assert contig(E=0) == 1
+
+    def masked(max_m=16, ws=1 << 20, E=8):
+        return L.chord_moe_dispatch_masked(FAKE, 4, 256, FAKE, 2, 0, E, max_m, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, ws, None)
+
+    assert masked(max_m=0) == 1
+    assert masked(ws=16) == 4
+    assert masked(E=1 << 20) in (1, 2)
+    assert L.chord_moe_combine(FAKE, 16, 100, FAKE, FAKE, 4, 2, FAKE, None) == 2
+    assert L.chord_moe_combine(FAKE, 16, 256, None, FAKE, 4, 2, FAKE, None) == 1
+    assert L.chord_moe_combine(FAKE, 1 << 22, 1024, FAKE, FAKE, 4, 2, FAKE, None) == 2
+    assert L.chord_moe_combine(FAKE, 16, 256, FAKE, FAKE, 0, 2, FAKE, None) == 0   # no tokens: no-op
