@@ -132,6 +132,74 @@ def algorithmic_work(wl):
 
 
 # ---------------------------------------------------------------------------
+# the steps either side of the grouped layer: dispatch and combine
+# ---------------------------------------------------------------------------
+
+def grouped_io(C, wl, rows, steps, dev, d, dbf):
+    """Average launch-stream time of the dispatch into both grouped layouts
+    (alignment included) and of the standalone combine, on the workload's
+    routing, with their algorithmic HBM bytes: each routed row read and
+    written once (2*H bytes each way; padding rows of the contiguous layout
+    are written), the routing ids read and the slot map written (4 B per
+    slot each); the combine reads each routed row and writes each token row."""
+    import torch
+    x, ids, w = dbf(wl.x), d(wl.topk_ids), d(wl.topk_weights)
+    T, k, H, E_l, eb = wl.T, wl.k, wl.H, wl.E_l, wl.expert_begin
+    flat = wl.topk_ids.reshape(-1) - eb
+    local = (flat >= 0) & (flat < E_l)
+    R = int(local.sum())
+    counts = np.bincount(flat[local], minlength=E_l)
+    padded = int((-(-counts // 128) * 128).sum())
+    max_rows = C.chord_moe_dispatch_contiguous_rows(T, k, E_l)
+    max_m = 256
+
+    ca = (torch.empty((max_rows, H), dtype=torch.bfloat16, device=dev),
+          torch.empty(max_rows, dtype=torch.int32, device=dev),
+          torch.empty(T * k, dtype=torch.int32, device=dev),
+          torch.empty(1, dtype=torch.int32, device=dev))
+    cws = torch.empty(C.chord_moe_dispatch_workspace_bytes(C.MODE_CONTIGUOUS, T, k, E_l),
+                      dtype=torch.uint8, device=dev)
+    ma = (torch.empty((E_l, max_m, H), dtype=torch.bfloat16, device=dev),
+          torch.empty(E_l, dtype=torch.int32, device=dev),
+          torch.empty(T * k, dtype=torch.int32, device=dev),
+          torch.empty(1, dtype=torch.int32, device=dev))
+    mws = torch.empty(C.chord_moe_dispatch_workspace_bytes(C.MODE_MASKED, T, k, E_l),
+                      dtype=torch.uint8, device=dev)
+    tok = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    C.chord_moe_dispatch_contiguous(x, ids, eb, E_l, max_rows, out=ca, workspace=cws)
+    torch.cuda.synchronize()
+    f2r = ca[2].clone()
+    kept = int(np.minimum(counts, max_m).sum())
+    calls = {
+        "dispatch_contiguous": (
+            lambda: C.chord_moe_dispatch_contiguous(x, ids, eb, E_l, max_rows, out=ca,
+                                                    workspace=cws),
+            2 * H * R + 2 * H * padded + 8 * T * k),
+        "dispatch_masked_maxm256": (
+            lambda: C.chord_moe_dispatch_masked(x, ids, eb, E_l, max_m, out=ma, workspace=mws),
+            4 * H * kept + 8 * T * k),
+        "combine": (lambda: C.chord_moe_combine(rows, f2r, w, out=tok),
+                    2 * H * R + 2 * H * T + 8 * T * k),
+    }
+    res = {}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "algorithmic_bytes": int(nbytes),
+                     "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    res["routed_rows"] = R
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
@@ -316,6 +384,9 @@ def main():
              "layer_TFLOPs": round(work["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
              "routed_rows": work["R"], "active_experts": work["active"], "plan": plan,
              "weight_replicas": n_rep}
+
+    if wl.layout == "contiguous":
+        extra["grouped_io"] = grouped_io(C, wl, out_rows, args.steps, dev, d, dbf)
 
     cpu = None
     if not args.no_cpu:

@@ -5,9 +5,10 @@
 // match of the expert id) and per-wave counts in LDS, so the order is the
 // ascending flat index and the result is deterministic.
 //
-// Small inputs (<= kAlignChunk entries) run in one workgroup; larger ones in
-// three launches: per-chunk histograms, one offsets workgroup, per-chunk
-// scatters.
+// Small inputs (<= kAlignSingle entries, <= 512 experts) run in one
+// workgroup; larger ones in two launches over chunks of >= kAlignMinChunk
+// entries: per-chunk histograms, then per-chunk scatters that derive their
+// offsets from the histograms themselves.
 #include "internal.h"
 
 namespace chord {
@@ -127,56 +128,102 @@ __global__ __launch_bounds__(1024) void align_single(AlignArgs a) {
 }
 
 // ---- multi-workgroup path -------------------------------------------------
-__global__ __launch_bounds__(256) void align_count(AlignArgs a) {
+// Two launches: per-chunk expert counts, then per-chunk scatters.  Each
+// scatter workgroup stages the whole [chunks, experts] count table in LDS and
+// derives from it every expert's padded segment start and its own chunk's
+// offset inside each segment, so no offsets launch sits between the two.  The
+// padding sentinels, the per-block expert ids, the padded total and the
+// buffer tails are written by the scatter workgroups between them.
+constexpr int kAlignThreads = 256;
+constexpr int kCountBatch = 4;
+
+__global__ __launch_bounds__(kAlignThreads) void align_count(AlignArgs a) {
   extern __shared__ int lds[];
   const int E = a.num_experts;
   for (int e = threadIdx.x; e < E; e += blockDim.x) lds[e] = 0;
   __syncthreads();
-  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
-  const int64_t end = min(a.n, begin + kAlignChunk);
-  for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
-    const int e = local_expert(a.topk_ids, i, a.n, a.expert_begin, E);
-    if (e >= 0) atomicAdd(&lds[e], 1);
+  const int64_t begin = (int64_t)blockIdx.x * a.chunk;
+  const int64_t end = min(a.n, begin + a.chunk);
+  for (int64_t base = begin; base < end; base += kAlignThreads * kCountBatch) {
+    int e[kCountBatch];
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u)
+      e[u] = local_expert(a.topk_ids, base + u * kAlignThreads + threadIdx.x, end,
+                          a.expert_begin, E);
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u)
+      if (e[u] >= 0) atomicAdd(&lds[e[u]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     a.chunk_counts[(int64_t)blockIdx.x * E + e] = lds[e];
 }
 
-__global__ __launch_bounds__(1024) void align_offsets(AlignArgs a) {
-  __shared__ int tmp[16];
-  const int E = a.num_experts;
-  const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E) {
-    for (int c = 0; c < a.nchunks; ++c) {
-      const int v = a.chunk_counts[(int64_t)c * E + e];
-      a.chunk_counts[(int64_t)c * E + e] = cnt;  // exclusive prefix over chunks
-      cnt += v;
-    }
-  }
-  const int padded = ((cnt + a.block_m - 1) / a.block_m) * a.block_m;
-  int total;
-  const int seg = block_exclusive_scan(padded, tmp, &total);
-  if (e < E) {
-    write_segment(e, seg, cnt, padded, a.block_m, (int32_t)a.n, a.sorted_ids, a.expert_ids);
-    a.seg_start[e] = seg;
-  }
-  if (threadIdx.x == 0) *a.ntpp = total;
-  fill_tail(total, a);
-}
-
-__global__ __launch_bounds__(256) void align_scatter(AlignArgs a) {
+__global__ __launch_bounds__(kAlignThreads) void align_scatter(AlignArgs a) {
   extern __shared__ int lds[];
-  const int E = a.num_experts;
-  int* running = lds;         // [E]
-  int* wcnt = lds + E;        // [4][E]
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    running[e] = a.seg_start[e] + a.chunk_counts[(int64_t)blockIdx.x * E + e];
+  const int E = a.num_experts, nc = a.nchunks, b = blockIdx.x, bm = a.block_m;
+  int* counts = lds;               // [nc][E]
+  int* running = counts + nc * E;  // [E]: next slot of each expert for this chunk
+  int* seg = running + E;          // [E + 1]: padded segment starts, seg[E] = total
+  int* wcnt = seg + E + 1;         // [4][E]
+  int* tmp = wcnt + 4 * E;         // [16]
+  for (int x = threadIdx.x; x < nc * E; x += blockDim.x) counts[x] = a.chunk_counts[x];
   for (int x = threadIdx.x; x < 4 * E; x += blockDim.x) wcnt[x] = 0;
   __syncthreads();
-  const int64_t begin = (int64_t)blockIdx.x * kAlignChunk;
-  const int64_t end = min(a.n, begin + kAlignChunk);
+  // Thread t owns experts [t*per, t*per + per): count over all chunks, count
+  // over the chunks before this one, then a workgroup scan of padded sizes.
+  const int per = (E + kAlignThreads - 1) / kAlignThreads;
+  const int e0 = threadIdx.x * per;
+  int mine = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = e0 + q;
+    if (e >= E) break;
+    int tot = 0, before = 0;
+    for (int c = 0; c < nc; ++c) {
+      const int v = counts[c * E + e];
+      before += c < b ? v : 0;
+      tot += v;
+    }
+    running[e] = before;
+    seg[e] = tot;
+    mine += (tot + bm - 1) / bm * bm;
+  }
+  int total;
+  int start = block_exclusive_scan(mine, tmp, &total);
+  const int32_t sentinel = (int32_t)a.n;
+  for (int q = 0; q < per; ++q) {
+    const int e = e0 + q;
+    if (e >= E) break;
+    const int cnt = seg[e];
+    const int padded = (cnt + bm - 1) / bm * bm;
+    if (e % nc == b)
+      for (int p = start + cnt; p < start + padded; ++p) a.sorted_ids[p] = sentinel;
+    seg[e] = start;
+    running[e] += start;
+    start += padded;
+  }
+  if (threadIdx.x == 0) seg[E] = total;
+  __syncthreads();
+  if (b == 0 && threadIdx.x == 0) *a.ntpp = total;
+  const int64_t gt = (int64_t)b * blockDim.x + threadIdx.x;
+  const int64_t gs = (int64_t)gridDim.x * blockDim.x;
+  const int64_t used_blocks = total / bm;
+  for (int64_t blk = gt; blk < used_blocks; blk += gs) {
+    // the expert whose segment holds row blk*bm: first i with seg[i] > row, minus one
+    const int64_t row = blk * bm;
+    int lo = 0, hi = E;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (seg[mid] > row) hi = mid;
+      else lo = mid + 1;
+    }
+    a.expert_ids[blk] = lo - 1;
+  }
+  const int64_t all_blocks = (a.max_padded + bm - 1) / bm;
+  for (int64_t blk = used_blocks + gt; blk < all_blocks; blk += gs) a.expert_ids[blk] = -1;
+  for (int64_t p = total + gt; p < a.max_padded; p += gs) a.sorted_ids[p] = sentinel;
+  const int64_t begin = (int64_t)b * a.chunk;
+  const int64_t end = min(a.n, begin + a.chunk);
   for (int64_t base = begin; base < end; base += blockDim.x)
     scatter_round(a.topk_ids, base + threadIdx.x, end, a.expert_begin, E, running, wcnt,
                   a.sorted_ids);
@@ -186,19 +233,17 @@ __global__ __launch_bounds__(256) void align_scatter(AlignArgs a) {
 
 hipError_t launch_align(const AlignArgs& a, hipStream_t stream) {
   const int E = a.num_experts;
-  if (a.n <= kAlignChunk && E <= 512) {
+  if (align_single_workgroup(a.n, E)) {
     const size_t lds = (size_t)(17 * E + 16) * sizeof(int);
     hipLaunchKernelGGL(align_single, dim3(1), dim3(1024), lds, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(align_count, dim3(a.nchunks), dim3(256), (size_t)E * sizeof(int), stream, a);
-  hipError_t err = hipGetLastError();
+  hipLaunchKernelGGL(align_count, dim3(a.nchunks), dim3(kAlignThreads), (size_t)E * sizeof(int),
+                     stream, a);
+  const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(align_offsets, dim3(1), dim3(1024), 0, stream, a);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(align_scatter, dim3(a.nchunks), dim3(256), (size_t)5 * E * sizeof(int), stream,
-                     a);
+  const size_t lds = ((size_t)a.nchunks * E + 6 * (size_t)E + 17) * sizeof(int);
+  hipLaunchKernelGGL(align_scatter, dim3(a.nchunks), dim3(kAlignThreads), lds, stream, a);
   return hipGetLastError();
 }
 

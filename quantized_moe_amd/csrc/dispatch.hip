@@ -19,14 +19,30 @@ __device__ __forceinline__ int64_t used_rows(const DispatchArgs& a) {
   return t < 0 ? 0 : (t > a.max_padded ? a.max_padded : t);
 }
 
-// Block-uniform row copy (or zero fill when src is null).
-__device__ __forceinline__ void copy_row(const uint16_t* src, uint16_t* dst, int nvec) {
+// Block-uniform row copy (or zero fill when src is null).  All loads of a
+// thread's pieces (up to 4 per 1024-piece span) are issued before the first
+// store, so each thread keeps several 16-byte loads in flight instead of one
+// dependent load/store pair at a time.
+constexpr int kThreads = 256;
+constexpr int kPieces = 4;
+
+__device__ __forceinline__ void copy_row(const uint16_t* __restrict__ src,
+                                         uint16_t* __restrict__ dst, int nvec) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
   uint4* d = reinterpret_cast<uint4*>(dst);
-  if (src) {
-    for (int v = threadIdx.x; v < nvec; v += blockDim.x) d[v] = s[v];
-  } else {
-    for (int v = threadIdx.x; v < nvec; v += blockDim.x) d[v] = make_uint4(0u, 0u, 0u, 0u);
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kThreads * kPieces) {
+    uint4 buf[kPieces];
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+      const int v = v0 + u * kThreads;
+      buf[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (src != nullptr && v < nvec) buf[u] = s[v];
+    }
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+      const int v = v0 + u * kThreads;
+      if (v < nvec) d[v] = buf[u];
+    }
   }
 }
 
@@ -39,7 +55,7 @@ __device__ __forceinline__ void mark_nonlocal(const DispatchArgs& a, int64_t gti
   }
 }
 
-__global__ __launch_bounds__(256) void gather_contiguous(DispatchArgs a) {
+__global__ __launch_bounds__(kThreads) void gather_contiguous(DispatchArgs a) {
   const int nvec = a.H >> 3;
   const int64_t n = (int64_t)a.T * a.k;
   const int64_t used = used_rows(a);
@@ -76,7 +92,7 @@ __global__ void clear_counter(int32_t* p) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
 }
 
-__global__ __launch_bounds__(256) void gather_masked(DispatchArgs a) {
+__global__ __launch_bounds__(kThreads) void gather_masked(DispatchArgs a) {
   const int nvec = a.H >> 3;
   const int64_t n = (int64_t)a.T * a.k;
   const int64_t used = used_rows(a);
@@ -119,8 +135,8 @@ unsigned dispatch_grid(int64_t rows) {
 }  // namespace
 
 hipError_t launch_gather_contiguous(const DispatchArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(gather_contiguous, dim3(dispatch_grid(a.max_padded)), dim3(256), 0, stream,
-                     a);
+  hipLaunchKernelGGL(gather_contiguous, dim3(dispatch_grid(a.max_padded)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -128,7 +144,8 @@ hipError_t launch_gather_masked(const DispatchArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(clear_counter, dim3(1), dim3(64), 0, stream, a.dropped);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gather_masked, dim3(dispatch_grid(a.max_padded)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(gather_masked, dim3(dispatch_grid(a.max_padded)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -153,8 +153,8 @@ struct AlignArgs {
   int32_t* sorted_ids;
   int32_t* expert_ids;
   int32_t* ntpp;
-  int32_t* chunk_counts;   // workspace [nchunks, E_l]
-  int32_t* seg_start;      // workspace [E_l]
+  int32_t* chunk_counts;   // workspace [nchunks, E_l] (multi-workgroup path)
+  int64_t chunk;           // entries per workgroup (multi-workgroup path)
   int nchunks;
 };
 
@@ -201,7 +201,24 @@ hipError_t launch_gather_contiguous(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_gather_masked(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_zero(uint16_t* p, int64_t n, hipStream_t stream);
 
-constexpr int kAlignChunk = 8192;       // entries per align workgroup
+constexpr int kAlignSingle = 8192;      // align in one workgroup up to this many entries
+constexpr int kAlignMinChunk = 1024;    // entries per align workgroup (at least)
+constexpr int kAlignCountCap = 8192;    // chunk x expert counts staged in LDS (about)
+
+// Entries per workgroup of the multi-workgroup alignment: small chunks for
+// many workgroups, large enough that the [chunks, experts] count table each
+// scatter workgroup stages in LDS stays near kAlignCountCap ints.
+inline int64_t align_chunk(int64_t n, int E) {
+  int64_t c = (n * E + kAlignCountCap - 1) / kAlignCountCap;
+  c = (c + 255) / 256 * 256;
+  return c < kAlignMinChunk ? kAlignMinChunk : c;
+}
+inline int64_t align_nchunks(int64_t n, int E) {
+  const int64_t c = align_chunk(n, E);
+  const int64_t m = (n + c - 1) / c;
+  return m < 1 ? 1 : m;
+}
+inline bool align_single_workgroup(int64_t n, int E) { return n <= kAlignSingle && E <= 512; }
 constexpr int kMaxExperts = 1024;       // E_l limit (LDS tables)
 constexpr int kMaxSegments = 16384;     // contiguous 128-row chunks limit
 

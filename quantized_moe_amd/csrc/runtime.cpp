@@ -762,8 +762,7 @@ size_t chord_moe_align_workspace_bytes(int T, int k, int num_local_experts, int 
   (void)block_m;
   if (T < 0 || k < 1 || num_local_experts < 1) return 0;
   const int64_t n = (int64_t)T * k;
-  const int64_t nchunks = (n + kAlignChunk - 1) / kAlignChunk;
-  return (size_t)(nchunks + 1) * num_local_experts * sizeof(int32_t) + 256;
+  return (size_t)align_nchunks(n, num_local_experts) * num_local_experts * sizeof(int32_t) + 256;
 }
 
 chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_begin,
@@ -788,7 +787,7 @@ chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_b
                 (long long)max_padded,
                 (long long)chord_moe_align_max_padded(T, k, num_local_experts, block_m));
   const size_t need = chord_moe_align_workspace_bytes(T, k, num_local_experts, block_m);
-  const bool single = n <= kAlignChunk && num_local_experts <= 512;
+  const bool single = align_single_workgroup(n, num_local_experts);
   if (!single && (!workspace || ws_bytes < need))
     return fail(CHORD_ERR_WORKSPACE, "align workspace %zu bytes, %zu needed", ws_bytes, need);
   CHORD_CHECK(check_device(nullptr));
@@ -802,15 +801,12 @@ chord_status chord_moe_align(const int32_t* topk_ids, int T, int k, int expert_b
   a.sorted_ids = sorted_ids;
   a.expert_ids = expert_ids;
   a.ntpp = num_tokens_post_padded;
-  a.nchunks = (int)((n + kAlignChunk - 1) / kAlignChunk);
-  if (a.nchunks == 0) a.nchunks = 1;
-  if (!single) {
-    a.seg_start = static_cast<int32_t*>(workspace);
-    a.chunk_counts = a.seg_start + num_local_experts;
-  }
+  a.chunk = align_chunk(n, num_local_experts);
+  a.nchunks = (int)align_nchunks(n, num_local_experts);
+  if (!single) a.chunk_counts = static_cast<int32_t*>(workspace);
   const hipError_t e = launch_align(a, static_cast<hipStream_t>(stream));
   HIP_TRY(e, "align launch");
-  g_last_plan = single ? "align: single workgroup" : "align: count/offsets/scatter";
+  g_last_plan = single ? "align: single workgroup" : "align: count/scatter";
   return CHORD_OK;
 }
 
