@@ -215,64 +215,100 @@ __global__ void clear_status(DevStatus* s) {
 // ---------------------------------------------------------------------------
 // Combine: out[t] = bf16(sum over slots j with a row, ascending j, of
 // w[t,j] * y_row), fp32 accumulation; tokens without a local slot get 0.
-// One thread per 8 output elements.
+// One wave per (token, span of 64 * 8 * kCombinePieces outputs): the token is
+// uniform across the wave, so the slot ids (or the slot -> row map) and the
+// weights are scalar loads and the per-batch branch is uniform.  Each lane
+// owns kCombinePieces 16-byte pieces (8 outputs each), and the row loads of
+// kCombineBatch slots are issued together, so a wave keeps several KiB in
+// flight.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+constexpr int kCombineWaves = 4;
+constexpr int kCombinePieces = 2;
+constexpr int kCombineBatch = 4;
+
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
+  constexpr int P = kCombinePieces, B = kCombineBatch;
   const int nvec = a.H / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)a.T * nvec) return;
-  const int t = (int)(idx / nvec);
-  const int v = (int)(idx % nvec);
-  // Rows through a buffer resource; the loads of up to 8 slots are issued
-  // together instead of one dependent branch at a time.  Products and sums
-  // keep ascending slot order.
+  const int spans = (nvec + 64 * P - 1) / (64 * P);
+  // T * spans < 2^31 (host-checked), so 32-bit wave indexing; every value
+  // below derived from `wid` is wave-uniform.
+  const int wid = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kCombineWaves +
+                                                 (int)(threadIdx.x >> 6));
+  if (wid >= a.T * spans) return;
+  const int t = __builtin_amdgcn_readfirstlane(wid / spans);
+  const int vbase = (wid - t * spans) * 64 * P + (int)(threadIdx.x & 63);
+  // Rows through a buffer resource (loads past its end return zeros).
   const int64_t row_bytes = (int64_t)a.H * 2;
   const int64_t span = a.n_rows * row_bytes;
   const __amdgpu_buffer_rsrc_t rres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)a.rows, 0, (int)(span < 0x7FFFFFFF ? span : 0x7FFFFFFF), 0x00020000);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < a.k; j0 += 8) {
-    uint32_t off[8];
-    float wj[8];
+  const int64_t s0 = (int64_t)t * a.k;
+  float acc[P][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u;
-      off[u] = 0xFFFFFFFFu;
-      wj[u] = 0.f;
-      if (j >= a.k) continue;
-      int64_t row;
-      if (a.flat_to_row != nullptr) {
-        row = a.flat_to_row[(int64_t)t * a.k + j];
-        if (row < 0 || row >= a.n_rows) continue;
-      } else {
-        const int e = a.topk_ids[(int64_t)t * a.k + j] - a.expert_begin;
-        if (e < 0 || e >= a.num_experts) continue;
-        row = (int64_t)t * a.k + j;
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[p][i] = 0.f;
+  for (int j0 = 0; j0 < a.k; j0 += B) {
+    // Unconditional (index-clamped) metadata loads first, so they batch.
+    int32_t raw[B];
+    float wj[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int j = j0 + u < a.k ? j0 + u : a.k - 1;
+      raw[u] = a.flat_to_row != nullptr ? a.flat_to_row[s0 + j] : a.topk_ids[s0 + j];
+      wj[u] = a.topk_weights[s0 + j];
+    }
+    int64_t row[B];
+    bool any = false;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      int64_t r = -1;
+      if (j0 + u < a.k) {
+        if (a.flat_to_row != nullptr) {
+          r = raw[u];
+          if (r >= a.n_rows) r = -1;
+        } else {
+          const int e = raw[u] - a.expert_begin;
+          r = (e >= 0 && e < a.num_experts) ? s0 + j0 + u : -1;
+        }
       }
-      off[u] = (uint32_t)(row * row_bytes + v * 16);
-      wj[u] = a.topk_weights[(int64_t)t * a.k + j];
+      row[u] = r;
+      any |= r >= 0;
     }
-    // A wave covers 512 consecutive outputs of (mostly) one token, so the
-    // guard is uniform and skips the loads of slots without a row.
-    u32x4_t y[8];
+    if (!any) continue;
+    // Slots without a row load from past the buffer's end (zeros) with weight
+    // 0: adding those +-0 products leaves every partial sum unchanged, and no
+    // load sits behind a branch.
+    u32x4_t y[B][P];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      y[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (off[u] != 0xFFFFFFFFu) y[u] = __builtin_amdgcn_raw_buffer_load_b128(rres, off[u], 0, 0);
-    }
+    for (int u = 0; u < B; ++u) {
+      if (row[u] < 0) wj[u] = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (off[u] == 0xFFFFFFFFu) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += wj[u] * bf16_to_f32(y[u][i] & 0xFFFFu);
-        acc[2 * i + 1] += wj[u] * bf16_to_f32(y[u][i] >> 16);
+      for (int p = 0; p < P; ++p) {
+        const int v = vbase + p * 64;
+        const uint32_t off = (row[u] >= 0 && v < nvec) ? (uint32_t)(row[u] * row_bytes + v * 16)
+                                                        : 0xFFFFFFF0u;
+        y[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0);
       }
     }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[p][2 * i] += wj[u] * bf16_to_f32(y[u][p][i] & 0xFFFFu);
+          acc[p][2 * i + 1] += wj[u] * bf16_to_f32(y[u][p][i] >> 16);
+        }
   }
-  const uint4 o = make_uint4(pk_bf16(acc[0], acc[1]), pk_bf16(acc[2], acc[3]),
-                             pk_bf16(acc[4], acc[5]), pk_bf16(acc[6], acc[7]));
-  *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.H + v * 8) = o;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int v = vbase + p * 64;
+    if (v >= nvec) continue;
+    const uint4 o = make_uint4(pk_bf16(acc[p][0], acc[p][1]), pk_bf16(acc[p][2], acc[p][3]),
+                               pk_bf16(acc[p][4], acc[p][5]), pk_bf16(acc[p][6], acc[p][7]));
+    *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.H + v * 8) = o;
+  }
 }
 
 __global__ void zero_kernel(uint16_t* p, int64_t n) {
@@ -300,8 +336,10 @@ hipError_t launch_check_blocks(const TileBuildArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  const int64_t n = (int64_t)a.T * (a.H / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  const int per_wave = 64 * kCombinePieces;
+  const int64_t waves = (int64_t)a.T * ((a.H / 8 + per_wave - 1) / per_wave);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((waves + kCombineWaves - 1) / kCombineWaves)),
+                     dim3(64 * kCombineWaves), 0, stream, a);
   return hipGetLastError();
 }
 
