@@ -132,6 +132,41 @@ def algorithmic_work(wl):
 
 
 # ---------------------------------------------------------------------------
+# the same step replayed from a HIP graph (launch-latency-bound small shapes)
+# ---------------------------------------------------------------------------
+
+def graph_replay_us(step, n_rep, steps):
+    """Captures one call per weight replica (alignment + layer, the timed step)
+    into a HIP graph and returns the average time per call over `steps`
+    replays, bracketed by HIP events on the capturing stream.  The layer's
+    default path enqueues no memset, no allocation and no host sync, so it is
+    capturable as is."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n_rep):       # plans and workspaces exist before capture
+            step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n_rep):
+            step(i)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / (steps * n_rep), 2)
+
+
+# ---------------------------------------------------------------------------
 # the steps either side of the grouped layer: dispatch and combine
 # ---------------------------------------------------------------------------
 
@@ -387,6 +422,8 @@ def main():
 
     if wl.layout == "contiguous":
         extra["grouped_io"] = grouped_io(C, wl, out_rows, args.steps, dev, d, dbf)
+    if wl.layout == "indexed" and wl.T <= 64:
+        extra["graph_us_per_call"] = graph_replay_us(step, n_rep, args.steps)
 
     cpu = None
     if not args.no_cpu:
