@@ -8,13 +8,18 @@ down GEMM, weighted combine) for the indexed layout; the layer alone for the
 grouped layouts (their row maps are the dispatcher's output).  Inputs are
 resident in HBM before the timed region.  Weight replicas are rotated across
 steps so that every step streams its weights from HBM, not from the 256 MB
-Infinity Cache.
+Infinity Cache.  Before the W warm-up steps, untimed steps run for at least
+--prewarm-ms (default 300 ms): the GPU raises its clocks over tens of
+milliseconds of sustained work, so without it the timed steps would measure
+the ramp (decode: about 221 instead of 193 µs per call), not the steady state
+of a busy serving loop.
 
 Prints ONE JSON line (rank 0).  `roofline` reports the dominant kernel
 (gate_up for decode-shaped calls, the bigger of the two GEMMs otherwise)
 against HBM (8 TB/s) or dense BF16 MFMA (2.5 PFLOP/s) from its algorithmic
 bytes / FLOPs and its average duration, measured with HIP events recorded by
-the library on the launch stream over the timed region.  `cpu_baseline` times
+the library on the launch stream over a second pass of the same K steps (event
+records between kernels would add microseconds to the timed pass itself).  `cpu_baseline` times
 the CPU oracle on a bounded sample of the same workload.
 """
 
@@ -48,6 +53,10 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="untimed steps for at least this long before the warm-up steps: the "
+                         "GPU's clocks ramp up over tens of ms of sustained work, and the timed "
+                         "steps should see the steady state a serving loop runs in")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="MIB",
                     help="instead of the layer, run `steps` plain device copies of MIB MiB "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
@@ -365,6 +374,15 @@ def main():
                   "H": wl.H, "I": wl.I, "expected_m": wl.expected_m,
                   "rows": int(wl.masked_m.sum())}
 
+    # Clock pre-warm (untimed), then the W warm-up steps (untimed).
+    prewarm_steps = 0
+    t_pre = time.perf_counter()
+    while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
+        for _ in range(8):
+            step(prewarm_steps)
+            prewarm_steps += 1
+        torch.cuda.synchronize()
+    prewarm_ms = (time.perf_counter() - t_pre) * 1e3
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -418,7 +436,8 @@ def main():
              "layer_hbm_GBs": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
              "layer_TFLOPs": round(work["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
              "routed_rows": work["R"], "active_experts": work["active"], "plan": plan,
-             "weight_replicas": n_rep}
+             "weight_replicas": n_rep,
+             "prewarm": {"ms": round(prewarm_ms, 1), "steps": prewarm_steps}}
 
     if wl.layout == "contiguous":
         extra["grouped_io"] = grouped_io(C, wl, out_rows, args.steps, dev, d, dbf)
