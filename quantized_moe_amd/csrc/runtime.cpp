@@ -247,12 +247,14 @@ Plan make_plan(const PlanKey& key) {
       g.nt = 2;
       if (chunks >= 16) g.wk = 4;
     }
-    // Nearly empty token tiles (a few rows per expert): the token loads of an
-    // item are mostly out-of-range zeros, so 2 weight tiles per item cost
-    // little extra and the smaller register set fits a fourth wave per SIMD
-    // (deep-K gate_up at decode: about 4 % faster; with denser tiles the
-    // doubled token loads per weight byte make it slower).
-    if (tok_e <= 4.0 && chunks >= 24) g.nt = 2;
+    // Nearly empty token tiles (a few rows per expert) on a wide, deep-K GEMM:
+    // the token loads of an item are mostly out-of-range zeros, so 2 weight
+    // tiles per item cost little extra and the smaller register set fits a
+    // fourth wave per SIMD (decode gate_up, N = 4096: 128 -> 121 us at steady
+    // clocks).  With denser tiles the doubled token loads per weight byte make
+    // it slower, and on the narrow TP-slice gate_up (N = 512) the doubled
+    // item count does (T = 32: 123 -> 128 us).
+    if (tok_e <= 4.0 && chunks >= 24 && N >= 2048) g.nt = 2;
     const int nt = ov_nt ? ov_nt : env_nt;
     const int wk = ov_wk ? ov_wk : env_wk;
     if (nt == 2 || nt == 4) g.nt = nt;
