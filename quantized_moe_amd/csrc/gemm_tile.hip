@@ -2,9 +2,12 @@
 // segments, hot masked experts): MFMA-bound, so every dequantised weight is
 // reused by up to 192 token rows.
 //
-// Workgroup = 4 waves (one per SIMD); wave w owns 4 consecutive 16-row weight
-// tiles (64 output rows), the workgroup a 256-row slice of one expert's
-// output.  A token tile of up to 192 rows is staged in LDS one 128-wide K
+// Workgroup = W waves (4: one per SIMD, or 8: two per SIMD); wave w owns
+// 16 / W consecutive 16-row weight tiles, the workgroup a 256-row slice of one
+// expert's output.  A single wave per SIMD cannot issue MFMAs back to back
+// (it saturates near 1.5 PFLOP/s on gfx950 whatever its number of independent
+// accumulators), two reach about 2.1 PFLOP/s; the 8-wave form gets there by
+// halving each wave's tiles (and registers) over the same LDS token stage.  A token tile of up to 192 rows is staged in LDS one 128-wide K
 // chunk at a time (double buffer, one barrier per chunk).  Each wave streams
 // its weight tiles straight from HBM into registers two chunks ahead,
 // dequantises them exactly (bf16_rne((q - 8) * s)) and issues
@@ -23,8 +26,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kNoRow = 0xC0000000u;  // byte offset past any token buffer
 constexpr int kStreamAux = 2;
 constexpr int kXcds = 8;
-constexpr int kWaves = 4;
-constexpr int kNT = 4;                        // weight tiles per wave
+constexpr int kWaves = 4;                     // short-K kernel: waves per workgroup
+constexpr int kNT = 4;                        // short-K kernel: weight tiles per wave
+constexpr int kSliceTiles = 16;               // 16-row weight tiles per 256-row slice
 constexpr int kMaxGroups = 12;                // 16-row token groups per tile (192 rows)
 constexpr int kXBufBytes = kMaxGroups * 16 * kChunkK * 2;  // one staged K chunk, 192 rows
 constexpr int kStages = 3;                    // token / weight buffers (two chunks in flight)
@@ -99,9 +103,11 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
 // piece (l % 16) ^ (r % 16) of row r = 4j + l / 16, so each row is still read
 // as one contiguous 256-byte run, and the MFMA B reads (16 rows, one piece
 // each) hit 16 distinct slots: no bank conflicts.
-template <int MG>
+template <int MG, int W>
 __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const int32_t* srcoff,
                                          const int64_t* dstrow, const float* roww, int e, int ng) {
+  constexpr int NT = kSliceTiles / W;  // weight tiles per wave
+  constexpr int kDma = 4 * MG / W;      // token DMA instructions per wave and chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -110,36 +116,37 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   const int nc = a.n_chunks;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // Wave w issues the DMA instructions j = w + 4 i (rows 4j .. 4j+3).
+  // Wave w issues the DMA instructions j = w + W i (rows 4j .. 4j+3); the
+  // lane's row is 4 w + q + 4 W i, so its row % 16 is (4 w + q) % 16.
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
-  const int rsub = 4 * wave + q;                 // row % 16 of this lane's rows
+  const int rsub = (4 * wave + q) & 15;          // row % 16 of this lane's rows
   const uint32_t pbytes = (uint32_t)((col ^ rsub) * 16);
-  uint32_t voff[MG];
+  uint32_t voff[kDma];
 #pragma unroll
-  for (int i = 0; i < MG; ++i) voff[i] = (uint32_t)srcoff[rsub + 16 * i] + pbytes;
+  for (int i = 0; i < kDma; ++i) voff[i] = (uint32_t)srcoff[4 * wave + q + 4 * W * i] + pbytes;
   auto load_x = [&](int slot, int c) {
 #pragma unroll
-    for (int i = 0; i < MG; ++i) {
-      uint8_t* dst = xbuf + slot * kXBufBytes + (wave + 4 * i) * 1024;
+    for (int i = 0; i < kDma; ++i) {
+      uint8_t* dst = xbuf + slot * kXBufBytes + (wave + W * i) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void*)dst, 16, voff[i], c * kChunkK * 2, 0, 0);
     }
   };
 
-  // Weights: kNT tiles of the slice per wave.  A wave past the last tile of
+  // Weights: NT tiles of the slice per wave.  A wave past the last tile of
   // a partial slice re-reads the slice's last tiles and stores nothing.
   const int64_t expert_bytes = (int64_t)a.n_tiles * nc * kBlockBytes;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
-  const int tile0 = (ng * kWaves + wave) * kNT;
+  const int tile0 = (ng * W + wave) * NT;
   const bool wave_live = tile0 < a.n_tiles;
-  const int tile_ld = wave_live ? tile0 : a.n_tiles - kNT;
-  uint4 wq[kStages][kNT];
-  uint32_t sc[kStages][kNT];
+  const int tile_ld = wave_live ? tile0 : a.n_tiles - NT;
+  uint4 wq[kStages][NT];
+  uint32_t sc[kStages][NT];
   auto load_w = [&](int slot, int c) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const uint32_t blk = (uint32_t)((tile_ld + nt) * nc + c) * kBlockBytes;
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
       wq[slot][nt] = make_uint4(v[0], v[1], v[2], v[3]);
@@ -147,9 +154,9 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
     }
   };
 
-  f32x4_t acc[kNT][MG];
+  f32x4_t acc[NT][MG];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int g = 0; g < MG; ++g) acc[nt][g] = zero4;
 
@@ -166,22 +173,22 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   // weights of the current step; the last step dequantises step 0 of the
   // next chunk from the weight slot `next`.  B reads do not cross the chunk
   // boundary: the next chunk's buffer is only valid after the barrier.
-  bf16x8_t av[kNT];
+  bf16x8_t av[NT];
   auto bread = [&](const uint8_t* xb, int st, int g) {
     return *reinterpret_cast<const bf16x8_t*>(xb + boff[st] + g * 16 * 256);
   };
   auto compute = [&](int slot, int next) {
     const uint8_t* xb = xbuf + slot * kXBufBytes;
-    DqScale ks[kNT];
+    DqScale ks[NT];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) ks[nt] = dq_scale(sc[slot][nt]);
+    for (int nt = 0; nt < NT; ++nt) ks[nt] = dq_scale(sc[slot][nt]);
     bf16x8_t bwin[3];
     bwin[0] = bread(xb, 0, 0);
     bwin[1] = MG > 1 ? bread(xb, 0, 1) : bread(xb, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      bf16x8_t an[kNT];
+      bf16x8_t an[NT];
 #pragma unroll
       for (int g = 0; g < MG; ++g) {
         const int idx = st * MG + g;
@@ -189,18 +196,18 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
         if (ahead < 4 * MG) bwin[ahead % 3] = bread(xb, ahead / MG, ahead % MG);
         const bf16x8_t bv = bwin[idx % 3];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
           acc[nt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nt], bv, acc[nt][g], 0, 0, 0);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          if (nt * MG / kNT != g) continue;
+        for (int nt = 0; nt < NT; ++nt) {
+          if (nt * MG / NT != g) continue;
           an[nt] = st < 3 ? dequant_word(word_of(wq[slot][nt], st + 1), ks[nt])
                           : dequant_word(wq[next][nt].x, dq_scale(sc[next][nt]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) av[nt] = an[nt];
+      for (int nt = 0; nt < NT; ++nt) av[nt] = an[nt];
     }
   };
 
@@ -209,12 +216,12 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   // (issued one chunk ago) has landed and pass the workgroup barrier.  The
   // barrier is a bare s_barrier with an explicit vmcnt wait: a fenced
   // __syncthreads would also wait for the x(c+2) DMA just issued.  Loads
-  // issued after x(c+1): w(c+1) (kNT x 2), x(c+2) (MG), w(c+2) (kNT x 2).
+  // issued after x(c+1): w(c+1) (NT x 2), x(c+2) (kDma), w(c+2) (NT x 2).
   // Prefetch indices are clamped instead of guarded so every iteration
   // issues the same loads (exact wait counts); the clamped re-reads at the
   // end hit the caches.
-  constexpr int kWLoads = 2 * kNT;
-  constexpr int kVm = MG + 2 * kWLoads;
+  constexpr int kWLoads = 2 * NT;
+  constexpr int kVm = kDma + 2 * kWLoads;
   constexpr int kWaitX = (kVm & 15) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14);
   auto chunk = [&](int slot, int c) {
     const int c2 = c + 2 < nc ? c + 2 : nc - 1;
@@ -238,7 +245,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) av[nt] = dequant_word(wq[0][nt].x, dq_scale(sc[0][nt]));
+  for (int nt = 0; nt < NT; ++nt) av[nt] = dequant_word(wq[0][nt].x, dq_scale(sc[0][nt]));
   int c = 0;
   for (; c + 2 < nc; c += 3) {
     chunk(0, c);
@@ -258,7 +265,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   for (int g = 0; g < MG; ++g) {
     const int64_t dr = dstrow[g * 16 + col];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       if (dr < 0) continue;
       const f32x4_t v = acc[nt][g];
       const int tw = tile0 + nt;
@@ -276,7 +283,8 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   }
 }
 
-__global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
+template <int W>
+__global__ __launch_bounds__(64 * W) void gemm_tile(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* xbuf = smem;                                                  // [3][192][256 B]
   int32_t* srcoff = reinterpret_cast<int32_t*>(smem + kStages * kXBufBytes);  // [192] byte offsets
@@ -323,12 +331,12 @@ __global__ __launch_bounds__(256) void gemm_tile(GemmArgs a) {
       // Live 16-row groups, rounded up to an even count.
       switch ((nrows + 31) >> 5) {
         case 0: break;
-        case 1: run_item<2>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 2: run_item<4>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 3: run_item<6>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 4: run_item<8>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 5: run_item<10>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        default: run_item<12>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 1: run_item<2, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 2: run_item<4, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 3: run_item<6, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 4: run_item<8, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        case 5: run_item<10, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        default: run_item<12, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
       }
       __syncthreads();  // row maps and LDS reuse by the next item
     }
@@ -575,14 +583,24 @@ hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
+  const int cus = a.num_cus > 0 ? a.num_cus : 256;
+  if (a.tile_waves == 8) {
+    static const int per_cu8 = [] {
+      hipFuncSetAttribute((const void*)gemm_tile<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kLdsBytes);
+      return blocks_per_cu(gemm_tile<8>, 512, kLdsBytes);
+    }();
+    if (grid > per_cu8 * cus) grid = per_cu8 * cus;
+    hipLaunchKernelGGL(gemm_tile<8>, dim3(grid), dim3(512), kLdsBytes, stream, a);
+    return hipGetLastError();
+  }
   static const int per_cu = [] {
-    hipFuncSetAttribute((const void*)gemm_tile, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipFuncSetAttribute((const void*)gemm_tile<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)kLdsBytes);
-    return blocks_per_cu(gemm_tile, 256, kLdsBytes);
+    return blocks_per_cu(gemm_tile<4>, 256, kLdsBytes);
   }();
-  const int cap = per_cu * (a.num_cus > 0 ? a.num_cus : 256);
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(gemm_tile, dim3(grid), dim3(256), kLdsBytes, stream, a);
+  if (grid > per_cu * cus) grid = per_cu * cus;
+  hipLaunchKernelGGL(gemm_tile<4>, dim3(grid), dim3(256), kLdsBytes, stream, a);
   return hipGetLastError();
 }
 

@@ -126,6 +126,7 @@ struct GemmArgs {
   int tiles_per_item;    // 16-row weight tiles per work item
   int items_per_tile;    // n_tiles / tiles_per_item (tiled kernel: 256-row slices)
   int slices_per_item;   // tiled kernel, K <= 256: consecutive slices per work item
+  int tile_waves;        // tiled kernel, K > 256: waves per workgroup (4 or 8)
   // output
   uint16_t* out;         // h [rows, I] (gate_up) or y / out rows [*, H] (down)
   int out_ld;

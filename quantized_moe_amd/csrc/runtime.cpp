@@ -87,6 +87,7 @@ struct EnvOverrides {
   int tokens = 0;
   int gu_nt = 0, gu_wk = 0, dn_nt = 0, dn_wk = 0;  // "nt,wk" per GEMM
   int tile_wgs = 0;  // tiled kernel: workgroups per CU
+  int tile_waves = 0;  // tiled kernel (K > 256): waves per workgroup, 4 or 8
   int stream_wgs = 0;  // streaming kernel: workgroups per CU (0: balanced default)
   int prefetch = 0;
   bool log = false;
@@ -99,6 +100,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_GATE_UP")) sscanf(s, "%d,%d", &o.gu_nt, &o.gu_wk);
     if (const char* s = getenv("CHORD_W4A16_DOWN")) sscanf(s, "%d,%d", &o.dn_nt, &o.dn_wk);
     if (const char* s = getenv("CHORD_W4A16_TILE_WGS")) o.tile_wgs = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_TILE_WAVES")) o.tile_waves = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_STREAM_WGS")) o.stream_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
@@ -138,6 +140,7 @@ struct GemmPlan {
   int wk;      // waves splitting K (streaming kernel)
   int pf;      // K chunks in flight per wave (streaming kernel)
   int grid;    // persistent workgroups
+  int waves;   // tiled kernel with K > 256: waves per workgroup (4 or 8)
 };
 // kernel: 1 = weight-streaming GEMMs on small tiles, 2 = LDS-tiled GEMMs on
 // big tiles, 3 = both, each expert going to one of them by its row count.
@@ -205,6 +208,9 @@ Plan make_plan(const PlanKey& key) {
       while (S > 1 && tiles_est * ((nslices + S - 1) / S) < 3.0 * key.cus) S = (S + 1) / 2;
     }
     g.slices = S;
+    // Two waves per SIMD (8 per workgroup, 2 weight tiles each): one wave
+    // cannot keep the MFMA pipe busy (prefill gate_up 486 -> 434 us).
+    g.waves = env().tile_waves == 4 ? 4 : 8;
     const int64_t items = (int64_t)p.max_tiles_b * ((nslices + S - 1) / S);
     const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 1;
     g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
@@ -292,8 +298,8 @@ Plan make_plan(const PlanKey& key) {
                   p.dn.nt, p.dn.wk, p.dn.pf, p.dn.slices);
   n = std::min(cap, n);
   if (kernel & 2)
-    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d (slices/item %d, %d)%s",
-             kTileTokens, p.gut.slices, p.dnt.slices,
+    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d, %d waves (slices/item %d, %d)%s",
+             kTileTokens, p.gut.waves, p.gut.slices, p.dnt.slices,
              kernel == 3 ? " for experts with >= 48 rows" : "");
   return p;
 }
@@ -469,6 +475,7 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   gt.items_per_tile = (g.n_tiles + gt.tiles_per_item - 1) / gt.tiles_per_item;
   gt.tile_tokens = kTileTokens;
   gt.slices_per_item = std::max(1, std::min(tp.slices, gt.items_per_tile));
+  gt.tile_waves = tp.waves;
   if (plan.kernel == 1) return launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream);
   if (plan.kernel == 2) return launch_gemm_tile(gt, tp.grid, stream);
   std::lock_guard<std::mutex> lk(g_side_mu);
