@@ -7,8 +7,9 @@
 // expert's output.  A single wave per SIMD cannot issue MFMAs back to back
 // (it saturates near 1.5 PFLOP/s on gfx950 whatever its number of independent
 // accumulators), two reach about 2.1 PFLOP/s; the 8-wave form gets there by
-// halving each wave's tiles (and registers) over the same LDS token stage.  A token tile of up to 192 rows is staged in LDS one 128-wide K
-// chunk at a time (double buffer, one barrier per chunk).  Each wave streams
+// halving each wave's tiles (and registers) over the same LDS token stage.
+// A token tile of up to 192 rows is staged in LDS one 128-wide K chunk at a
+// time (three buffers, one barrier per chunk).  Each wave streams
 // its weight tiles straight from HBM into registers two chunks ahead,
 // dequantises them exactly (bf16_rne((q - 8) * s)) and issues
 // v_mfma_f32_16x16x32_bf16 with the weights as A and the staged tokens as B.
@@ -75,6 +76,9 @@ struct RowMap {
   int64_t src;
   int64_t dst;
 };
+// LDS swizzle key of a token row (row % 16 -> a permutation of 0..15).
+__device__ __forceinline__ int swz(int r16) { return ((r16 & 7) << 1) | (r16 >> 3); }
+
 __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t R) {
   RowMap m{-1, -1};
   if (a.layout == kIndexed) {
@@ -99,10 +103,14 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
 // Token staging goes straight from memory to LDS (buffer_load ... lds): one
 // instruction moves 4 token rows x 256 bytes (one K chunk) into 1 KB of LDS
 // in lane order.  LDS row r holds the row's 16-byte pieces permuted by
-// slot = piece ^ (r % 16); lane l of the instruction for rows 4j..4j+3 fetches
-// piece (l % 16) ^ (r % 16) of row r = 4j + l / 16, so each row is still read
-// as one contiguous 256-byte run, and the MFMA B reads (16 rows, one piece
-// each) hit 16 distinct slots: no bank conflicts.
+// slot = piece ^ swz(r % 16); lane l of the instruction for rows 4j..4j+3
+// fetches piece (l % 16) ^ swz(r % 16) of row r = 4j + l / 16, so each row is
+// still read as one contiguous 256-byte run.  The MFMA B reads (16 rows, one
+// piece each) then hit 16 distinct slots, and the key swz(r) = 2 (r % 8) +
+// r / 8 also spreads rows r and r + 8 over different bank halves: gfx950
+// serves a 128-bit LDS read in 8-byte halves, 16 lanes at a time, and a plain
+// piece ^ r leaves those 16 lanes on 8 bank pairs (2-way conflicts; measured
+// 143 vs 245 bytes per clock per CU).
 template <int MG, int W>
 __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const int32_t* srcoff,
                                          const int64_t* dstrow, const float* roww, int e, int ng) {
@@ -121,7 +129,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
   const int rsub = (4 * wave + q) & 15;          // row % 16 of this lane's rows
-  const uint32_t pbytes = (uint32_t)((col ^ rsub) * 16);
+  const uint32_t pbytes = (uint32_t)((col ^ swz(rsub)) * 16);
   uint32_t voff[kDma];
 #pragma unroll
   for (int i = 0; i < kDma; ++i) voff[i] = (uint32_t)srcoff[4 * wave + q + 4 * W * i] + pbytes;
@@ -163,7 +171,8 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   // B operand of group g, step st: token row g*16 + col, piece q*4 + st.
   uint32_t boff[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ col) * 16));
+  for (int st = 0; st < 4; ++st)
+    boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ swz(col)) * 16));
 
   // One chunk, software-pipelined by hand (scheduling fences keep the order):
   // the chunk is 4 MFMA steps x MG token groups; each group section issues
@@ -366,7 +375,7 @@ __device__ __forceinline__ void run_item_shortk(const GemmArgs& a, uint8_t* xbuf
     const __amdgpu_buffer_rsrc_t xres =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
     const int rsub = 4 * wave + q;
-    const uint32_t pbytes = (uint32_t)((col ^ rsub) * 16);
+    const uint32_t pbytes = (uint32_t)((col ^ swz(rsub)) * 16);
 #pragma unroll
     for (int i = 0; i < MG; ++i) {
       const uint32_t voff = (uint32_t)srcoff[rsub + 16 * i] + pbytes;
@@ -403,7 +412,8 @@ __device__ __forceinline__ void run_item_shortk(const GemmArgs& a, uint8_t* xbuf
   f32x4_t acc[kNT][MG];
   uint32_t boff[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ col) * 16));
+  for (int st = 0; st < 4; ++st)
+    boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ swz(col)) * 16));
 
   // One slice: NC chunks x 4 MFMA steps over MG token groups, B reads two
   // groups ahead, the next step's dequantisation spread over the groups
