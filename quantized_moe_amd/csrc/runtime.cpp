@@ -162,7 +162,9 @@ std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 
 constexpr int kTileSlice = 256;    // output rows per workgroup of the tiled kernel
 constexpr int kTileTokens = 192;   // token rows per big tile (tiled kernel)
-constexpr double kTileMinRows = 48.0;
+constexpr double kTileMinRows = 24.0;        // auto choice of the tiled family
+constexpr double kTileMinRowsShortK = 8.0;   // same, when the down GEMM is short-K
+constexpr double kSplitRows = 48.0;          // kernel 3: experts with this many rows go tiled
 
 int max_tiles_for(int64_t rows, int E_l, int tile_tokens) {
   return (int)((rows + tile_tokens - 1) / tile_tokens) + E_l + 1;
@@ -187,10 +189,18 @@ Plan make_plan(const PlanKey& key) {
   p.cus = key.cus;
   const bool tile_ok = (2 * key.I) % 64 == 0 && key.H % 64 == 0;  // 4 tiles per wave
   int kernel = key.ov[0] ? key.ov[0] : env().kernel;
-  if (kernel < 1 || kernel > 3) kernel = tok_e >= kTileMinRows ? 2 : 1;
+  if (kernel < 1 || kernel > 3) {
+    // Expected rows per expert decide the family (measured crossovers on
+    // MI355X at steady clocks): the tiled kernel from 24 rows, or from 8 when
+    // the down GEMM is short-K (I <= 256: token tile resident in LDS, several
+    // slices per item; TP slice T = 512: 328 -> 294 us; masked E = 24, 31
+    // rows: 266 -> 246 us; masked E = 48, 18 rows, stays streaming).
+    const double cross = key.I <= 256 ? kTileMinRowsShortK : kTileMinRows;
+    kernel = tok_e >= cross ? 2 : 1;
+  }
   if (!tile_ok) kernel = 1;
   p.kernel = kernel;
-  p.split_rows = kernel == 3 ? (int)kTileMinRows : (kernel == 2 ? 0 : INT32_MAX);
+  p.split_rows = kernel == 3 ? (int)kSplitRows : (kernel == 2 ? 0 : INT32_MAX);
   p.max_tiles_b = kernel & 2 ? max_tiles_for(key.rows, key.E_l, kTileTokens) : 0;
 
   // Tiled GEMMs: one workgroup per CU (registers, ~150 KB of LDS); the
@@ -222,7 +232,7 @@ Plan make_plan(const PlanKey& key) {
   }
 
   // Streaming GEMMs.
-  const double tok_small = kernel == 3 ? std::min(tok_e, kTileMinRows - 1) : tok_e;
+  const double tok_small = kernel == 3 ? std::min(tok_e, kSplitRows - 1) : tok_e;
   int mt = (int)((tok_small + 15.0) / 16.0);
   mt = std::max(1, std::min(2, mt));
   const int tokens = key.ov[1] ? key.ov[1] : env().tokens;
