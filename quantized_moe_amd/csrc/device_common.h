@@ -57,6 +57,43 @@ __device__ inline int block_scan_excl(int v, int* tmp, int* total) {
   return base + x - v;
 }
 
+// Exclusive scans of N ints per thread across the workgroup at once (same
+// contract as block_scan_excl; `tmp` holds >= 16 * N ints of LDS): v[i]
+// becomes the exclusive prefix of counter i, total[i] its sum.  Two barriers
+// for all N counters instead of two per counter.
+template <int N>
+__device__ inline void block_scan_excl_n(int (&v)[N], int* tmp, int (&total)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = v[i];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int y = __shfl_up(x[i], d, 64);
+      if (lane >= d) x[i] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) tmp[wave * N + i] = x[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int base = 0, sum = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = tmp[w * N + i];
+      if (w < wave) base += t;
+      sum += t;
+    }
+    v[i] = base + x[i] - v[i];
+    total[i] = sum;
+  }
+  __syncthreads();
+}
+
 // Resident workgroups per CU of a kernel.
 template <typename K>
 inline int blocks_per_cu(K kernel, int threads, size_t lds) {

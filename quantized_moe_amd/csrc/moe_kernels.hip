@@ -20,7 +20,7 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
   __shared__ int first[kMaxExperts];
   __shared__ int last[kMaxExperts];
   __shared__ int nblk[kMaxExperts];
-  __shared__ int tmp[16];
+  __shared__ int scan_tmp[16 * 9];
   __shared__ int err;
   const int tid = threadIdx.x;
   const int E = a.num_experts;
@@ -86,9 +86,26 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
     __syncthreads();
     if (tid < E && last[tid] >= 0) {
       if (a.validate && last[tid] - first[tid] + 1 != nblk[tid]) atomicOr(&err, 16);
+      // Last row of this expert in its last chunk: the chunk's 128 ids are
+      // read as 32 independent 16-byte loads, all in flight together (4-byte
+      // loads if the caller's m_indices is not 16-byte aligned).
+      const int32_t* ids = a.m_indices + (int64_t)last[tid] * 128;
       int lastv = 0;
-      for (int r = 0; r < 128; ++r)
-        if (a.m_indices[(int64_t)last[tid] * 128 + r] == tid) lastv = r + 1;
+      if ((reinterpret_cast<uintptr_t>(ids) & 15) == 0) {
+        int4 v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = reinterpret_cast<const int4*>(ids)[i];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (v[i].x == tid) lastv = 4 * i + 1;
+          if (v[i].y == tid) lastv = 4 * i + 2;
+          if (v[i].z == tid) lastv = 4 * i + 3;
+          if (v[i].w == tid) lastv = 4 * i + 4;
+        }
+      } else {
+        for (int r = 0; r < 128; ++r)
+          if (ids[r] == tid) lastv = r + 1;
+      }
       nblk[tid] = (last[tid] - first[tid]) * 128 + lastv;  // segment rows
     }
   }
@@ -127,14 +144,19 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
       cnt_small += (rows + TOK - 1) / TOK;
     }
   });
-  int total_small;
-  int base_small = block_scan_excl(cnt_small, tmp, &total_small);
+  // One workgroup scan of the 9 counters (small tiles, 8 size classes).
+  int cnt[kBuckets + 1], tot[kBuckets + 1];
+  cnt[kBuckets] = cnt_small;
+#pragma unroll
+  for (int b = 0; b < kBuckets; ++b) cnt[b] = cntb[b];
+  block_scan_excl_n<kBuckets + 1>(cnt, scan_tmp, tot);
+  const int total_small = tot[kBuckets];
+  int base_small = cnt[kBuckets];
   int rank[kBuckets];
   int total_big = 0;
   for (int b = kBuckets - 1; b >= 0; --b) {  // biggest class first
-    int tot;
-    rank[b] = total_big + block_scan_excl(cntb[b], tmp, &tot);
-    total_big += tot;
+    rank[b] = total_big + cnt[b];
+    total_big += tot[b];
   }
   const bool big_fits = total_big <= a.max_tiles_b;
   if ((total_small > a.max_tiles || !big_fits) && a.validate && tid == 0) atomicOr(&err, 64);
