@@ -115,7 +115,7 @@ template <int MG, int W>
 __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const int32_t* srcoff,
                                          const int64_t* dstrow, const float* roww, int e, int ng) {
   constexpr int NT = kSliceTiles / W;  // weight tiles per wave
-  constexpr int kDma = 4 * MG / W;      // token DMA instructions per wave and chunk
+  constexpr int kDma = (4 * MG + W - 1) / W;  // token DMA instructions per wave and chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,19 +124,24 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   const int nc = a.n_chunks;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // Wave w issues the DMA instructions j = w + W i (rows 4j .. 4j+3); the
-  // lane's row is 4 w + q + 4 W i, so its row % 16 is (4 w + q) % 16.
+  // Wave w issues the DMA instructions j = w + W i (rows 4j .. 4j+3).  When
+  // W does not divide 4 MG, the surplus slots repeat the last row block
+  // (j = 4 MG - 1): an identical copy, same source and same LDS bytes, so
+  // every wave issues kDma loads and the wait counts below stay exact.
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
-  const int rsub = (4 * wave + q) & 15;          // row % 16 of this lane's rows
-  const uint32_t pbytes = (uint32_t)((col ^ swz(rsub)) * 16);
   uint32_t voff[kDma];
+  int jblk[kDma];
 #pragma unroll
-  for (int i = 0; i < kDma; ++i) voff[i] = (uint32_t)srcoff[4 * wave + q + 4 * W * i] + pbytes;
+  for (int i = 0; i < kDma; ++i) {
+    jblk[i] = min(wave + W * i, 4 * MG - 1);
+    const int row = 4 * jblk[i] + q;
+    voff[i] = (uint32_t)srcoff[row] + (uint32_t)((col ^ swz(row & 15)) * 16);
+  }
   auto load_x = [&](int slot, int c) {
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
-      uint8_t* dst = xbuf + slot * kXBufBytes + (wave + W * i) * 1024;
+      uint8_t* dst = xbuf + slot * kXBufBytes + jblk[i] * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void*)dst, 16, voff[i], c * kChunkK * 2, 0, 0);
     }
@@ -337,14 +342,15 @@ __global__ __launch_bounds__(64 * W) void gemm_tile(GemmArgs a) {
       }
       __syncthreads();
 
-      // Live 16-row groups, rounded up to an even count.
-      switch ((nrows + 31) >> 5) {
+      // Live 16-row groups (a 171-row tile computes 176 rows, not 192).
+      switch ((nrows + 15) >> 4) {
         case 0: break;
-        case 1: run_item<2, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 2: run_item<4, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 3: run_item<6, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 4: run_item<8, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
-        case 5: run_item<10, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+#define CHORD_TILE_CASE(MG) \
+  case MG: run_item<MG, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        CHORD_TILE_CASE(1) CHORD_TILE_CASE(2) CHORD_TILE_CASE(3) CHORD_TILE_CASE(4)
+        CHORD_TILE_CASE(5) CHORD_TILE_CASE(6) CHORD_TILE_CASE(7) CHORD_TILE_CASE(8)
+        CHORD_TILE_CASE(9) CHORD_TILE_CASE(10) CHORD_TILE_CASE(11)
+#undef CHORD_TILE_CASE
         default: run_item<12, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
       }
       __syncthreads();  // row maps and LDS reuse by the next item
