@@ -110,7 +110,10 @@ typedef struct {
   int32_t down_nt;     /* as above for the down GEMM */
   int32_t down_wk;
   int32_t prefetch;    /* K chunks in flight per wave: 2 or 4; 0 auto */
-  int32_t reserved;
+  int32_t tile_split;  /* 1: no K split of outsized tiles in the tiled GEMMs (each output is
+                          then summed over K in one pass, in chunk order); 0 auto: a tile
+                          with far more rows than the call's mean is split along K into up
+                          to 4 parts whose fp32 partials the last part adds in part order */
 } chord_schedule;
 
 /* ---------------------------------------------------------------------------

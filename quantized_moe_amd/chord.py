@@ -52,7 +52,7 @@ class Schedule(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tokens", ctypes.c_int32),
                 ("gate_up_nt", ctypes.c_int32), ("gate_up_wk", ctypes.c_int32),
                 ("down_nt", ctypes.c_int32), ("down_wk", ctypes.c_int32),
-                ("prefetch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("prefetch", ctypes.c_int32), ("tile_split", ctypes.c_int32)]
 
 
 def _load():
@@ -213,8 +213,7 @@ def _sched(override):
         return None
     s = Schedule()
     for name, _ in Schedule._fields_:
-        if name != "reserved":
-            setattr(s, name, int(override.get(name, 0)))
+        setattr(s, name, int(override.get(name, 0)))
     return ctypes.byref(s)
 
 

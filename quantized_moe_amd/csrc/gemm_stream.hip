@@ -122,7 +122,7 @@ __device__ __forceinline__ int num_tiles(const GemmArgs& a) {
 __device__ __forceinline__ TileDesc get_tile(const GemmArgs& a, int ti) {
   if (a.tiles != nullptr) return a.tiles[ti];
   const int e = a.expert_ids[ti];
-  TileDesc t{e, ti * a.block_m, a.block_m, 0};
+  TileDesc t{e, ti * a.block_m, a.block_m, 0, 1, 0, 0, 0};
   if (e < 0 || e >= a.num_experts) t.expert = -1;
   return t;
 }

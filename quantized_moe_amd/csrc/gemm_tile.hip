@@ -113,7 +113,9 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
 // 143 vs 245 bytes per clock per CU).
 template <int MG, int W>
 __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const int32_t* srcoff,
-                                         const int64_t* dstrow, const float* roww, int e, int ng) {
+                                         const int64_t* dstrow, const float* roww,
+                                         const TileDesc& td, int ng) {
+  const int e = td.expert;
   constexpr int NT = kSliceTiles / W;  // weight tiles per wave
   constexpr int kDma = (4 * MG + W - 1) / W;  // token DMA instructions per wave and chunk
   const int tid = threadIdx.x;
@@ -121,7 +123,10 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4;
   const int col = lane & 15;
-  const int nc = a.n_chunks;
+  // K range of this entry: part kpart of ksplit (the whole K when unsplit).
+  const int c_lo = td.kpart * a.n_chunks / td.ksplit;
+  const int c_hi = (td.kpart + 1) * a.n_chunks / td.ksplit;  // end of the range
+  const int nc = a.n_chunks;  // chunks per weight tile (block stride)
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // Wave w issues the DMA instructions j = w + W i (rows 4j .. 4j+3).  When
@@ -238,7 +243,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   constexpr int kVm = kDma + 2 * kWLoads;
   constexpr int kWaitX = (kVm & 15) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14);
   auto chunk = [&](int slot, int c) {
-    const int c2 = c + 2 < nc ? c + 2 : nc - 1;
+    const int c2 = c + 2 < c_hi ? c + 2 : c_hi - 1;
     const int fill = slot == 0 ? 2 : slot - 1;
     load_x(fill, c2);
     load_w(fill, c2);
@@ -250,9 +255,9 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int c1 = nc > 1 ? 1 : 0;
-  load_x(0, 0);
-  load_w(0, 0);
+  const int c1 = c_lo + 1 < c_hi ? c_lo + 1 : c_lo;
+  load_x(0, c_lo);
+  load_w(0, c_lo);
   load_x(1, c1);
   load_w(1, c1);
   __builtin_amdgcn_s_waitcnt(kWaitX);  // x(0) landed
@@ -260,17 +265,32 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) av[nt] = dequant_word(wq[0][nt].x, dq_scale(sc[0][nt]));
-  int c = 0;
-  for (; c + 2 < nc; c += 3) {
+  int c = c_lo;
+  for (; c + 2 < c_hi; c += 3) {
     chunk(0, c);
     chunk(1, c + 1);
     chunk(2, c + 2);
   }
-  if (c < nc) chunk(0, c);
-  if (c + 1 < nc) chunk(1, c + 1);
+  if (c < c_hi) chunk(0, c);
+  if (c + 1 < c_hi) chunk(1, c + 1);
   // Drain the clamped prefetches (DMA into LDS) before the buffers are
   // reused by the next item.
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+
+  // K split: each part only stores its fp32 accumulators to its partial
+  // slot (lane-linear, i.e. the register layout, indexed by the tile's place
+  // in the slice); the fixup kernel that follows this launch on the stream
+  // adds the parts in part order and runs the epilogue.
+  if (td.ksplit > 1) {
+    if (!wave_live) return;
+    f32x4_t* mine = reinterpret_cast<f32x4_t*>(
+        a.partials + (size_t)(td.pbase + (td.kpart * a.max_slices + ng) * MG) * kPartialSlotFloats);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int g = 0; g < MG; ++g) mine[((wave * NT + nt) * MG + g) * 64 + lane] = acc[nt][g];
+    return;
+  }
 
   // Epilogue: lane holds rows 4q..4q+3 of weight tile nt for token col of
   // group g.
@@ -346,12 +366,12 @@ __global__ __launch_bounds__(64 * W) void gemm_tile(GemmArgs a) {
       switch ((nrows + 15) >> 4) {
         case 0: break;
 #define CHORD_TILE_CASE(MG) \
-  case MG: run_item<MG, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+  case MG: run_item<MG, W>(a, xbuf, srcoff, dstrow, roww, td, ng); break;
         CHORD_TILE_CASE(1) CHORD_TILE_CASE(2) CHORD_TILE_CASE(3) CHORD_TILE_CASE(4)
         CHORD_TILE_CASE(5) CHORD_TILE_CASE(6) CHORD_TILE_CASE(7) CHORD_TILE_CASE(8)
         CHORD_TILE_CASE(9) CHORD_TILE_CASE(10) CHORD_TILE_CASE(11)
 #undef CHORD_TILE_CASE
-        default: run_item<12, W>(a, xbuf, srcoff, dstrow, roww, e, ng); break;
+        default: run_item<12, W>(a, xbuf, srcoff, dstrow, roww, td, ng); break;
       }
       __syncthreads();  // row maps and LDS reuse by the next item
     }
@@ -585,7 +605,66 @@ __global__ __launch_bounds__(256) void gemm_tile_shortk(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// K-split fixup: one workgroup per (split tile, 256-row slice, weight tile t
+// of the slice); wave w handles the token groups g = w, w + 4, w + 8 of the
+// tile.  Lane (q, col) reads its f32x4 of every part (all loads in flight
+// together), adds them in part order and applies the same epilogue as the
+// GEMM.  The parts stored the layout index (t * MG + g) * 64 + lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tile_split_fixup(GemmArgs a) {
+  const int nslices = a.items_per_tile;
+  const int t = blockIdx.x % kSliceTiles;
+  const int ng = (blockIdx.x / kSliceTiles) % nslices;
+  const int sid = blockIdx.x / (kSliceTiles * nslices);
+  if (sid >= a.status->nsplit) return;
+  const int tw = ng * kSliceTiles + t;  // tile of the GEMM
+  if (tw >= a.n_tiles) return;
+  const TileDesc td = a.split_tiles[sid];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 4, col = lane & 15;
+  const int nrows = td.nrows < kMaxGroups * 16 ? td.nrows : kMaxGroups * 16;
+  const int MG = (nrows + 15) >> 4;
+  for (int g = wave; g < MG; g += 4) {
+    const int m = g * 16 + col;
+    int64_t dr = -1;
+    if (m < nrows) dr = map_row(a, td.expert, (int64_t)td.row_begin + m).dst;
+    f32x4_t part[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      part[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (p < td.ksplit)
+        part[p] = reinterpret_cast<const f32x4_t*>(
+            a.partials + (size_t)(td.pbase + (p * a.max_slices + ng) * MG) *
+                             kPartialSlotFloats)[(t * MG + g) * 64 + lane];
+    }
+    if (dr < 0) continue;
+    f32x4_t v = part[0];
+#pragma unroll
+    for (int p = 1; p < 4; ++p)
+      if (p < td.ksplit) v += part[p];
+    if (a.gate_up) {
+      const int f0 = tw * 8 + 2 * q;
+      *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
+          pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
+    } else {
+      const float rw = a.row_weights != nullptr ? a.row_weights[dr] : 1.0f;
+      const int n0 = tw * 16 + 4 * q;
+      *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
+          make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_split_fixup(const GemmArgs& a, hipStream_t stream) {
+  const int slices = a.items_per_tile;
+  hipLaunchKernelGGL(tile_split_fixup, dim3((unsigned)(kMaxSplitTiles * slices * kSliceTiles)),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream) {
   if (a.n_chunks <= 2) {  // short K: token tile resident, several slices per item

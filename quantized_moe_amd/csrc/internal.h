@@ -44,14 +44,24 @@ inline size_t packed_bytes(int E, int N, int K) {
   return (size_t)E * (size_t)(N / kTileRows) * (size_t)(K / kChunkK) * (size_t)kBlockBytes;
 }
 
-// Tile descriptor produced on the device: {local expert, first internal row,
-// number of internal rows (<= tile tokens), unused}.
+// Tile descriptor produced on the device: local expert, first internal row,
+// number of internal rows (<= tile tokens).  Big tiles may be split along K:
+// entry kpart of ksplit covers chunks [kpart nc / ksplit, (kpart + 1) nc /
+// ksplit); split_id indexes the call's split tiles and pbase is the tile's
+// first partial slot (one slot = 256 rows x 16 tokens of fp32).
 struct TileDesc {
   int32_t expert;
   int32_t row_begin;
   int32_t nrows;
+  int32_t kpart;
+  int32_t ksplit;
+  int32_t split_id;
+  int32_t pbase;
   int32_t pad;
 };
+constexpr int kMaxSplitTiles = 16;     // tiles split along K per layer call
+constexpr int kSplitCapSlots = 4096;   // partial slots (16 KB each: 64 MB)
+constexpr int kPartialSlotFloats = 256 * 16;
 
 enum Layout : int { kIndexed = 0, kContiguous = 1, kMasked = 2 };
 
@@ -61,7 +71,8 @@ struct DevStatus {
   int32_t error;                        // nonzero: routing validation failed (bit flags)
   int32_t ntiles;                       // tiles written by the tile builder
   int32_t group_start[kTileGroups + 1]; // tile range of each expert group
-  int32_t pad[53];
+  int32_t nsplit;                       // big tiles split along K
+  int32_t pad[52];
 };
 
 // Arguments of the tile builder (one workgroup).  Each expert segment goes
@@ -79,6 +90,10 @@ struct TileBuildArgs {
   int max_tiles_b;     // capacity of `tiles_b`
   int split_rows;      // segments with >= split_rows rows go to `tiles_b`
   int validate;
+  int split_cap;       // partial slots for K-split big tiles (0: no split)
+  int max_ksplit;      // parts per split tile (2..4)
+  int max_slices;      // 256-row slices of the wider tiled GEMM
+  TileDesc* split_tiles;  // [kMaxSplitTiles]: part-0 entry of each split tile
   // indexed
   const int32_t* expert_ids;
   const int32_t* ntpp;
@@ -127,6 +142,9 @@ struct GemmArgs {
   int items_per_tile;    // n_tiles / tiles_per_item (tiled kernel: 256-row slices)
   int slices_per_item;   // tiled kernel, K <= 256: consecutive slices per work item
   int tile_waves;        // tiled kernel, K > 256: waves per workgroup (4 or 8)
+  float* partials;       // tiled kernel: K-split partial slots
+  const TileDesc* split_tiles;  // tiled kernel: the split tiles (fixup pass)
+  int max_slices;        // slot stride of the tile builder
   // output
   uint16_t* out;         // h [rows, I] (gate_up) or y / out rows [*, H] (down)
   int out_ld;
@@ -197,6 +215,7 @@ hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArg
 // LDS-tiled GEMM (needs a device tile list with tiles of at most 192 rows;
 // 4 weight tiles per wave, 256 output rows per workgroup; N a multiple of 64).
 hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_tile_split_fixup(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_gather_contiguous(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_gather_masked(const DispatchArgs& a, hipStream_t stream);

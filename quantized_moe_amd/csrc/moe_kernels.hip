@@ -20,7 +20,7 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
   __shared__ int first[kMaxExperts];
   __shared__ int last[kMaxExperts];
   __shared__ int nblk[kMaxExperts];
-  __shared__ int scan_tmp[16 * 9];
+  __shared__ int scan_tmp[16 * 11];
   __shared__ int err;
   const int tid = threadIdx.x;
   const int E = a.num_experts;
@@ -129,29 +129,71 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
   // (k / 8 even ? k % 8 : 7 - k % 8) at position k / 8 of that group.  All
   // slices of one big tile stay in one group, so its token rows are read
   // into one XCD's L2.
+  //
+  // K split: a big tile with g live 16-row groups, well above the mean gm of
+  // the call's big tiles, becomes s = round(g / gm) entries (at most 4, and
+  // at most one per 8 K chunks of the shorter GEMM), each
+  // covering 1/s of K; the parts store fp32 partials and a fixup pass after
+  // the GEMM adds them.  One oversized tile (a hot expert) then stops setting
+  // the kernel's critical path.  Off when the partial slots or the split-tile
+  // list would overflow their caps.
   constexpr int kBuckets = 8;  // 32-row size classes (big tiles <= 256 rows)
   const int TOKB = a.big_tokens;
   auto is_big = [&](int rows) { return rows >= a.split_rows; };
   auto bucket = [&](int rows) { return min(kBuckets - 1, (rows - 1) >> 5); };
-  int cnt_small = 0;
-  int cntb[kBuckets];
-#pragma unroll
-  for (int b = 0; b < kBuckets; ++b) cntb[b] = 0;
+  auto groups_of = [](int n) { return (n + 15) >> 4; };
+
+  // Mean live groups of the big tiles.
+  int nbig_t = 0, gsum_t = 0;
   for_each_segment([&](int, int, int rows) {
-    if (is_big(rows)) {
-      for (int r = 0; r < rows; r += TOKB) ++cntb[bucket(min(TOKB, rows - r))];
-    } else {
-      cnt_small += (rows + TOK - 1) / TOK;
+    if (!is_big(rows)) return;
+    for (int r = 0; r < rows; r += TOKB) {
+      ++nbig_t;
+      gsum_t += groups_of(min(TOKB, rows - r));
     }
   });
-  // One workgroup scan of the 9 counters (small tiles, 8 size classes).
-  int cnt[kBuckets + 1], tot[kBuckets + 1];
-  cnt[kBuckets] = cnt_small;
+  int mean_in[2] = {nbig_t, gsum_t}, mean_tot[2];
+  block_scan_excl_n<2>(mean_in, scan_tmp, mean_tot);
+  bool split_on = a.split_cap > 0 && mean_tot[0] > 0;
+  auto ksplit_of = [&](int g) {
+    if (!split_on) return 1;
+    const int s = (2 * g * mean_tot[0] + mean_tot[1]) / (2 * mean_tot[1]);  // round(g / gm)
+    return s < 2 ? 1 : (s > a.max_ksplit ? a.max_ksplit : s);
+  };
+
+  // Counters: 8 size classes of big entries, small tiles, split tiles, and
+  // split units (sum of s * g over split tiles).
+  constexpr int kNC = kBuckets + 3;
+  int cnt[kNC], tot[kNC];
+  auto count_all = [&]() {
 #pragma unroll
-  for (int b = 0; b < kBuckets; ++b) cnt[b] = cntb[b];
-  block_scan_excl_n<kBuckets + 1>(cnt, scan_tmp, tot);
+    for (int i = 0; i < kNC; ++i) cnt[i] = 0;
+    for_each_segment([&](int, int, int rows) {
+      if (is_big(rows)) {
+        for (int r = 0; r < rows; r += TOKB) {
+          const int n = min(TOKB, rows - r), g = groups_of(n), sp = ksplit_of(g);
+          for (int p = 0; p < sp; ++p) ++cnt[bucket((n + sp - 1) / sp)];
+          if (sp > 1) {
+            ++cnt[kBuckets + 1];
+            cnt[kBuckets + 2] += sp * g;
+          }
+        }
+      } else {
+        cnt[kBuckets] += (rows + TOK - 1) / TOK;
+      }
+    });
+    block_scan_excl_n<kNC>(cnt, scan_tmp, tot);
+  };
+  count_all();
+  if (split_on && (tot[kBuckets + 1] > kMaxSplitTiles ||
+                   (int64_t)tot[kBuckets + 2] * a.max_slices > a.split_cap)) {
+    split_on = false;  // uniform across the workgroup: the totals are
+    count_all();
+  }
   const int total_small = tot[kBuckets];
   int base_small = cnt[kBuckets];
+  int split_id = cnt[kBuckets + 1];
+  int split_units = cnt[kBuckets + 2];
   int rank[kBuckets];
   int total_big = 0;
   for (int b = kBuckets - 1; b >= 0; --b) {  // biggest class first
@@ -191,16 +233,22 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
     if (is_big(rows)) {
       if (!big_fits) return;
       for (int r = 0; r < rows; r += TOKB) {
-        const int n = min(TOKB, rows - r);
-        const int k = rank[bucket(n)]++;
-        const int pos = k % kTileGroups, rnd = k / kTileGroups;
-        const int g = (rnd & 1) ? kTileGroups - 1 - pos : pos;
-        a.tiles_b[gstart[g] + rnd] = TileDesc{e, row_begin + r, n, 0};
+        const int n = min(TOKB, rows - r), g = groups_of(n), sp = ksplit_of(g);
+        const int sid = sp > 1 ? split_id++ : 0;
+        const int pbase = sp > 1 ? split_units * a.max_slices : 0;
+        if (sp > 1) split_units += sp * g;
+        for (int p = 0; p < sp; ++p) {
+          const int k = rank[bucket((n + sp - 1) / sp)]++;
+          const int pos = k % kTileGroups, rnd = k / kTileGroups;
+          const int grp = (rnd & 1) ? kTileGroups - 1 - pos : pos;
+          a.tiles_b[gstart[grp] + rnd] = TileDesc{e, row_begin + r, n, p, sp, sid, pbase, 0};
+        }
+        if (sp > 1) a.split_tiles[sid] = TileDesc{e, row_begin + r, n, 0, sp, sid, pbase, 0};
       }
     } else {
       for (int r = 0; r < rows; r += TOK) {
         if (base_small < a.max_tiles)
-          a.tiles[base_small] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0};
+          a.tiles[base_small] = TileDesc{e, row_begin + r, min(TOK, rows - r), 0, 1, 0, 0, 0};
         ++base_small;
       }
     }
@@ -208,6 +256,7 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
   __syncthreads();
   if (tid == 0) {
     a.status->ntiles = min(total_small, a.max_tiles);
+    a.status->nsplit = split_on && big_fits ? tot[kBuckets + 1] : 0;
     a.status->error = err;
   }
 }

@@ -88,6 +88,7 @@ struct EnvOverrides {
   int gu_nt = 0, gu_wk = 0, dn_nt = 0, dn_wk = 0;  // "nt,wk" per GEMM
   int tile_wgs = 0;  // tiled kernel: workgroups per CU
   int tile_waves = 0;  // tiled kernel (K > 256): waves per workgroup, 4 or 8
+  int tile_split = 0;  // tiled kernel: 1 turns the K split of outsized tiles off
   int stream_wgs = 0;  // streaming kernel: workgroups per CU (0: balanced default)
   int prefetch = 0;
   bool log = false;
@@ -101,6 +102,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_DOWN")) sscanf(s, "%d,%d", &o.dn_nt, &o.dn_wk);
     if (const char* s = getenv("CHORD_W4A16_TILE_WGS")) o.tile_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_TILE_WAVES")) o.tile_waves = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_TILE_SPLIT")) o.tile_split = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_STREAM_WGS")) o.stream_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
@@ -112,7 +114,8 @@ const EnvOverrides& env() {
 // ---- planner and plan cache ------------------------------------------------
 struct PlanKey {
   int mode, T, k, E_g, E_l, H, I, hint, cus;
-  int ov[7];  // schedule override fields (kernel, tokens, gu_nt, gu_wk, dn_nt, dn_wk, prefetch)
+  int ov[8];  // schedule override fields (kernel, tokens, gu_nt, gu_wk, dn_nt, dn_wk, prefetch,
+              // tile_split)
   int64_t rows;
   bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(*this)) == 0; }
 };
@@ -125,6 +128,7 @@ void fill_override(PlanKey& key, const chord_schedule* s) {
   key.ov[4] = s->down_nt;
   key.ov[5] = s->down_wk;
   key.ov[6] = s->prefetch;
+  key.ov[7] = s->tile_split;
 }
 struct PlanKeyHash {
   size_t operator()(const PlanKey& k) const {
@@ -152,6 +156,7 @@ struct Plan {
   int max_tiles;     // small-tile list capacity
   int max_tiles_b;   // big-tile list capacity
   int split_rows;    // kernel 3: experts with >= split_rows rows take the tiled kernel
+  bool tile_ksplit;  // tiled kernel: outsized tiles may be split along K
   int cus;
   GemmPlan gu, dn;    // streaming GEMMs
   GemmPlan gut, dnt;  // tiled GEMMs
@@ -193,15 +198,25 @@ Plan make_plan(const PlanKey& key) {
     // Expected rows per expert decide the family (measured crossovers on
     // MI355X at steady clocks): the tiled kernel from 24 rows, or from 8 when
     // the down GEMM is short-K (I <= 256: token tile resident in LDS, several
-    // slices per item; TP slice T = 512: 328 -> 294 us; masked E = 24, 31
-    // rows: 266 -> 246 us; masked E = 48, 18 rows, stays streaming).
-    const double cross = key.I <= 256 ? kTileMinRowsShortK : kTileMinRows;
+    // slices per item; TP slice T = 512: 328 -> 294 us; masked Zipf with
+    // the K split: E = 24 246 -> ~227, E = 48 389 -> ~331, E = 96 547 -> ~509).
+    // Masked calls split outsized tiles along K (below), which removes the
+    // hot-expert tail that made the tiled family lose on skewed counts.
+    const double cross =
+        (key.I <= 256 || key.mode == kMasked) ? kTileMinRowsShortK : kTileMinRows;
     kernel = tok_e >= cross ? 2 : 1;
   }
   if (!tile_ok) kernel = 1;
   p.kernel = kernel;
   p.split_rows = kernel == 3 ? (int)kSplitRows : (kernel == 2 ? 0 : INT32_MAX);
   p.max_tiles_b = kernel & 2 ? max_tiles_for(key.rows, key.E_l, kTileTokens) : 0;
+  // K split of outsized big tiles (masked layout: budgets per expert with
+  // skewed counts): both tiled GEMMs must run the general tiled kernel
+  // (K > 256; the short-K kernel has no split), and no override or
+  // environment switch may have turned it off.  It costs a fixup launch
+  // after each tiled GEMM, so near-uniform layouts do without.
+  p.tile_ksplit = (kernel & 2) && key.mode == kMasked && key.H / kChunkK > 2 &&
+                  key.I / kChunkK > 2 && key.ov[7] != 1 && env().tile_split != 1;
 
   // Tiled GEMMs: one workgroup per CU (registers, ~150 KB of LDS); the
   // launcher clamps to the occupancy it measures.
@@ -370,14 +385,16 @@ struct StageTimer {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, tiles, tiles_b, h, y, total;
-  int max_tiles, max_tiles_b;
+  size_t status, tiles, tiles_b, split_tiles, partials, h, y, total;
+  int max_tiles, max_tiles_b, max_slices;
 };
 
 WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   WsLayout w{};
   w.max_tiles = max_tiles_for(rows, E_l, 16);
-  w.max_tiles_b = max_tiles_for(rows, E_l, kTileTokens);
+  // Big tiles, plus up to 3 extra entries per K-split tile.
+  w.max_tiles_b = max_tiles_for(rows, E_l, kTileTokens) + 3 * kMaxSplitTiles;
+  w.max_slices = (std::max(2 * I, H) + kTileSlice - 1) / kTileSlice;
   size_t off = 0;
   w.status = off;
   off = align_up(off + sizeof(DevStatus), 256);
@@ -385,6 +402,10 @@ WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   off = align_up(off + (size_t)w.max_tiles * sizeof(TileDesc), 256);
   w.tiles_b = off;
   off = align_up(off + (size_t)w.max_tiles_b * sizeof(TileDesc), 256);
+  w.split_tiles = off;
+  off = align_up(off + (size_t)kMaxSplitTiles * sizeof(TileDesc), 256);
+  w.partials = off;
+  off = align_up(off + (size_t)kSplitCapSlots * kPartialSlotFloats * sizeof(float), 256);
   w.h = off;
   off = align_up(off + (size_t)rows * I * 2, 256);
   w.y = off;
@@ -487,14 +508,20 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   gt.slices_per_item = std::max(1, std::min(tp.slices, gt.items_per_tile));
   gt.tile_waves = tp.waves;
   if (plan.kernel == 1) return launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream);
-  if (plan.kernel == 2) return launch_gemm_tile(gt, tp.grid, stream);
+  // The tiled GEMM, then (K split on) the pass that completes split tiles.
+  auto tiled = [&](hipStream_t st) {
+    hipError_t e = launch_gemm_tile(gt, tp.grid, st);
+    if (e == hipSuccess && plan.tile_ksplit && gt.n_chunks > 2) e = launch_tile_split_fixup(gt, st);
+    return e;
+  };
+  if (plan.kernel == 2) return tiled(stream);
   std::lock_guard<std::mutex> lk(g_side_mu);
   SideStream* ss = nullptr;
   hipError_t e;
   if ((e = get_side(&ss)) != hipSuccess) return e;
   if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
-  if ((e = launch_gemm_tile(gt, tp.grid, ss->s)) != hipSuccess) return e;
+  if ((e = tiled(ss->s)) != hipSuccess) return e;
   if ((e = launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream)) != hipSuccess)
     return e;
   if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
@@ -523,7 +550,16 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   tb.tile_tokens = plan.tile_tokens;
   tb.max_tiles = std::min(plan.max_tiles, ws.max_tiles);
   tb.big_tokens = kTileTokens;
-  tb.max_tiles_b = std::min(plan.max_tiles_b, ws.max_tiles_b);
+  tb.max_tiles_b = plan.tile_ksplit ? ws.max_tiles_b : std::min(plan.max_tiles_b, ws.max_tiles_b);
+  tb.split_cap = plan.tile_ksplit ? kSplitCapSlots : 0;
+  // Parts of at least 8 K chunks in the shorter GEMM (shorter parts spend
+  // more on their prologue than they gain), 2..4; the environment (2..4)
+  // overrides for experiments.
+  tb.max_ksplit = env().tile_split >= 2 && env().tile_split <= 4
+                      ? env().tile_split
+                      : std::max(2, std::min(4, std::min(H, I) / kChunkK / 8));
+  tb.max_slices = ws.max_slices;
+  tb.split_tiles = reinterpret_cast<TileDesc*>(wsp + ws.split_tiles);
   tb.split_rows = plan.split_rows;
   tb.tiles = tiles;
   tb.tiles_b = tiles_b;
@@ -550,6 +586,9 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.max_padded = tb.max_padded;
   g.num_experts = tb.num_experts;
   g.num_cus = plan.cus;
+  g.partials = reinterpret_cast<float*>(wsp + ws.partials);
+  g.split_tiles = tb.split_tiles;
+  g.max_slices = ws.max_slices;
   g.tile_tokens = plan.tile_tokens;
   g.n_rows_internal = rows_internal;
 
@@ -986,7 +1025,7 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
     if (!in(override->kernel, {0, 1, 2, 3}) || !in(override->tokens, {0, 16, 32}) ||
         !in(override->gate_up_nt, {0, 2, 4}) || !in(override->down_nt, {0, 2, 4}) ||
         !in(override->gate_up_wk, {0, 1, 2, 4}) || !in(override->down_wk, {0, 1, 2, 4}) ||
-        !in(override->prefetch, {0, 2, 4}))
+        !in(override->prefetch, {0, 2, 4}) || !in(override->tile_split, {0, 1}))
       return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
   }
   const WsLayout ws = layer_ws(kIndexed, T, k, E_l, H, I, max_padded);

@@ -372,7 +372,7 @@ def test_tile_kernel_bit_identical_to_streaming_kernel():
     bit; several 128-row tiles per expert and ragged tails."""
     banner("tile kernel vs streaming kernel: indexed T=300 H=512 I=256")
     case = small_case(301, 300, 512, 256, 16, 8, 4, 4)
-    tiled, layer, _ = run_indexed(*case, E_g=16, bm=16, override={"kernel": 2})
+    tiled, layer, _ = run_indexed(*case, E_g=16, bm=16, override={"kernel": 2, "tile_split": 1})
     stream, _, _ = run_indexed(*case, E_g=16, bm=16, layer=layer,
                                override={"kernel": 1, "gate_up_wk": 1, "down_wk": 1})
     assert np.array_equal(tiled, stream)
@@ -423,7 +423,7 @@ def test_split_kernels_indexed_bit_identical_and_oracle():
     case = skewed_case(77, 256, 512, 256, 8, 2, [40, 20, 10, 5, 3, 2, 1, 1])
     counts = np.bincount(case[1].ravel(), minlength=8)
     assert counts.max() > 192 and (counts >= 48).sum() >= 2 and (counts < 48).sum() >= 2, counts
-    split, layer, _ = run_indexed(*case, E_g=8, bm=16, override={"kernel": 3})
+    split, layer, _ = run_indexed(*case, E_g=8, bm=16, override={"kernel": 3, "tile_split": 1})
     assert "experts with >= 48 rows" in C.last_plan()
     stream, _, _ = run_indexed(*case, E_g=8, bm=16, layer=layer,
                                override={"kernel": 1, "gate_up_wk": 1, "down_wk": 1})
@@ -501,3 +501,30 @@ def test_indexed_layer_replays_in_a_hip_graph(kernel):
         assert np.array_equal(replayed, host_bf16(eager_out)), f"replay {r}"
         check_close(replayed, oracle.moe_layer(case[0], case[1], case[2], base[3], base[4],
                                                base[5], base[6], 0), f"replay {r}")
+
+
+def test_tile_k_split_of_a_hot_expert_is_deterministic_and_close():
+    """A masked call with one expert far above the others: the tile builder
+    splits that expert's tiles along K and the last part adds the fp32
+    partials in part order, so repeats are bit-identical; the result matches
+    the oracle and the unsplit indexed path (same rows) within tolerance."""
+    from quantized_moe_amd.moe import W4A16MoE
+    banner("tiled K split: masked hot expert")
+    rng = np.random.default_rng(35)
+    E, max_m, H, I = 8, 192, 512, 512
+    a3, _, _, _ = G.draw_masked(rng, E, max_m, H)
+    mm = np.array([192, 9, 12, 7, 16, 5, 11, 8], np.int32)   # mean 16 groups 2.5, hot 12
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H, scale_mult=(256.0 / H) ** 0.5)
+    q2, s2 = G.draw_weights(rng, E, H, I, scale_mult=(256.0 / I) ** 0.5)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_MASKED)
+    outs = []
+    for _ in range(3):
+        o = layer.masked(dev_bf16(a3), dev(mm), 32)    # hint >= 24 rows: tiled kernel
+        torch.cuda.synchronize()
+        outs.append(host_bf16(o))
+    assert "tile" in C.last_plan()
+    ref = oracle.grouped_masked(a3, mm, q13, s13, q2, s2)
+    for e in range(E):    # rows past masked_m[e] are unspecified: compare valid rows only
+        sl = slice(e * max_m, e * max_m + mm[e])
+        assert np.array_equal(outs[0][sl], outs[1][sl]) and np.array_equal(outs[0][sl], outs[2][sl])
+        check_close(outs[0][sl], ref[sl], f"masked e={e}")
