@@ -97,6 +97,41 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
   return m;
 }
 
+// Down epilogue: y = acc * row weight, bf16.  Lane (q, col) holds outputs
+// 4q .. 4q+3 of each weight tile for token col; lanes exchange packed halves
+// (cross-lane reads) so that each lane stores 16 contiguous bytes: lane q
+// takes tile 2i + q / 2, outputs 8 (q % 2) .. 8 (q % 2) + 7, from lanes
+// 2 (q % 2) and 2 (q % 2) + 1 of its token.  Stores of 16 instead of 8 bytes
+// per lane (32 -> 64 contiguous bytes per token row) made the short-K down
+// GEMM of the I = 256 slices 17 % faster.
+template <int NT, int MG>
+__device__ __forceinline__ void store_down_pairs(const GemmArgs& a, const f32x4_t (&acc)[NT][MG],
+                                                 const int64_t* dstrow, const float* roww,
+                                                 int tile0, int q, int col) {
+  static_assert(NT % 2 == 0, "tile pairs");
+  const int src0 = ((2 * q) & 3) * 16 + col, src1 = src0 + 16;
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    const int64_t dr = dstrow[g * 16 + col];
+    const float rw = roww[g * 16 + col];
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      const f32x4_t v0 = acc[2 * i][g], v1 = acc[2 * i + 1][g];
+      const uint32_t p0x = pk_bf16(v0[0] * rw, v0[1] * rw), p0y = pk_bf16(v0[2] * rw, v0[3] * rw);
+      const uint32_t p1x = pk_bf16(v1[0] * rw, v1[1] * rw), p1y = pk_bf16(v1[2] * rw, v1[3] * rw);
+      const uint32_t a0 = __shfl(p0x, src0), a1 = __shfl(p0y, src0);
+      const uint32_t a2 = __shfl(p0x, src1), a3 = __shfl(p0y, src1);
+      const uint32_t b0 = __shfl(p1x, src0), b1 = __shfl(p1y, src0);
+      const uint32_t b2 = __shfl(p1x, src1), b3 = __shfl(p1y, src1);
+      if (dr < 0) continue;
+      const int tw = tile0 + 2 * i + (q >> 1);
+      const int n0 = tw * 16 + (q & 1) * 8;
+      *reinterpret_cast<uint4*>(a.out + dr * (int64_t)a.out_ld + n0) =
+          q < 2 ? make_uint4(a0, a1, a2, a3) : make_uint4(b0, b1, b2, b3);
+    }
+  }
+}
+
 // One work item: token tile of MG live 16-row groups x one 256-row slice.
 // srcoff / dstrow (LDS) already hold the tile's row maps.
 //
@@ -295,6 +330,10 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   // Epilogue: lane holds rows 4q..4q+3 of weight tile nt for token col of
   // group g.
   if (!wave_live) return;
+  if (!a.gate_up) {
+    store_down_pairs<NT, MG>(a, acc, dstrow, roww, tile0, q, col);
+    return;
+  }
 #pragma unroll
   for (int g = 0; g < MG; ++g) {
     const int64_t dr = dstrow[g * 16 + col];
@@ -303,16 +342,9 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
       if (dr < 0) continue;
       const f32x4_t v = acc[nt][g];
       const int tw = tile0 + nt;
-      if (a.gate_up) {
-        const int f0 = tw * 8 + 2 * q;
-        *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
-            pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
-      } else {
-        const int n0 = tw * 16 + 4 * q;
-        const float rw = roww[g * 16 + col];
-        *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
-            make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
-      }
+      const int f0 = tw * 8 + 2 * q;
+      *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
+          pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
     }
   }
 }
@@ -497,6 +529,10 @@ __device__ __forceinline__ void run_item_shortk(const GemmArgs& a, uint8_t* xbuf
   auto epilogue = [&](int s) {
     const int tile0 = tile_first(s);
     if (tile0 >= a.n_tiles) return;
+    if (!a.gate_up) {
+      store_down_pairs<kNT, MG>(a, acc, dstrow, roww, tile0, q, col);
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < MG; ++g) {
       const int64_t dr = dstrow[g * 16 + col];
