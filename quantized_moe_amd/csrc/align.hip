@@ -9,7 +9,7 @@
 // workgroup; larger ones in two launches over chunks of >= kAlignMinChunk
 // entries: per-chunk histograms, then per-chunk scatters that derive their
 // offsets from the histograms themselves.
-#include "internal.h"
+#include "device_common.h"
 
 namespace chord {
 namespace {
@@ -21,37 +21,22 @@ __device__ __forceinline__ int local_expert(const int32_t* ids, int64_t i, int64
   return (g >= 0 && g < E) ? g : -1;
 }
 
-// Exclusive scan of one int per thread across the workgroup (blockDim.x a
-// multiple of 64, at most 1024).  `tmp` holds >= 16 ints of LDS.  Returns the
-// exclusive prefix; *total receives the sum.
+// Exclusive scan of one int per thread across the workgroup; `tmp` holds
+// >= 17 ints of LDS.  Returns the exclusive prefix; *total receives the sum.
 __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  int base = 0, sum = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int t = tmp[w];
-    if (w < wave) base += t;
-    sum += t;
-  }
-  __syncthreads();
-  *total = sum;
-  return base + x - v;
+  int x[1] = {v}, t[1];
+  block_scan_excl_n<1>(x, tmp, t);
+  *total = t[0];
+  return x[0];
 }
 
-// One round: every thread takes entry i (ascending with the thread index) and
-// writes it to its stable position running[e] + (earlier entries of e in this
-// round).  `wcnt` is [waves][E] of zeros on entry and on exit.
-__device__ void scatter_round(const int32_t* __restrict__ ids, int64_t i, int64_t n, int eb, int E,
-                              int* running, int* wcnt, int32_t* __restrict__ sorted_ids) {
+// One round: every thread takes entry i (ascending with the thread index),
+// whose local expert e (-1: none) the caller has loaded, and writes it to its
+// stable position running[e] + (earlier entries of e in this round).  `wcnt`
+// is [waves][E] of zeros on entry and on exit.
+__device__ void scatter_round(int e, int64_t i, int E, int* running, int* wcnt,
+                              int32_t* __restrict__ sorted_ids) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = local_expert(ids, i, n, eb, E);
   const bool valid = e >= 0;
   uint64_t mask = __ballot(valid);
 #pragma unroll
@@ -100,14 +85,20 @@ __global__ __launch_bounds__(1024) void align_single(AlignArgs a) {
   const int E = a.num_experts;
   int* running = lds;              // [E]
   int* wcnt = lds + E;             // [16][E]
-  int* tmp = lds + 17 * E;         // [16]
+  int* tmp = lds + 17 * E;         // [17]
   for (int e = threadIdx.x; e < E; e += blockDim.x) running[e] = 0;
   for (int x = threadIdx.x; x < 16 * E; x += blockDim.x) wcnt[x] = 0;
+  // n <= kAlignSingle = 8 x 1024: every thread loads its (up to) 8 entries
+  // once, all in flight together, and keeps them for the scatter rounds.
+  constexpr int kPer = kAlignSingle / 1024;
+  int ev[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    ev[u] = local_expert(a.topk_ids, (int64_t)u * blockDim.x + threadIdx.x, a.n, a.expert_begin, E);
   __syncthreads();
-  for (int64_t i = threadIdx.x; i < a.n; i += blockDim.x) {
-    const int e = local_expert(a.topk_ids, i, a.n, a.expert_begin, E);
-    if (e >= 0) atomicAdd(&running[e], 1);
-  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (ev[u] >= 0) atomicAdd(&running[ev[u]], 1);
   __syncthreads();
   // E <= 1024 = blockDim: thread e owns expert e.
   const int e = threadIdx.x;
@@ -122,9 +113,12 @@ __global__ __launch_bounds__(1024) void align_single(AlignArgs a) {
   if (threadIdx.x == 0) *a.ntpp = total;
   fill_tail(total, a);
   __syncthreads();
-  for (int64_t base = 0; base < a.n; base += blockDim.x)
-    scatter_round(a.topk_ids, base + threadIdx.x, a.n, a.expert_begin, E, running, wcnt,
-                  a.sorted_ids);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t base = (int64_t)u * blockDim.x;
+    if (base >= a.n) break;  // uniform
+    scatter_round(ev[u], base + threadIdx.x, E, running, wcnt, a.sorted_ids);
+  }
 }
 
 // ---- multi-workgroup path -------------------------------------------------
@@ -136,6 +130,8 @@ __global__ __launch_bounds__(1024) void align_single(AlignArgs a) {
 // buffer tails are written by the scatter workgroups between them.
 constexpr int kAlignThreads = 256;
 constexpr int kCountBatch = 4;
+constexpr int kStageBatch = 8;  // count-table loads in flight per thread
+constexpr int kIdBatch = 8;     // scatter rounds whose entries load together
 
 __global__ __launch_bounds__(kAlignThreads) void align_count(AlignArgs a) {
   extern __shared__ int lds[];
@@ -166,8 +162,31 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter(AlignArgs a) {
   int* running = counts + nc * E;  // [E]: next slot of each expert for this chunk
   int* seg = running + E;          // [E + 1]: padded segment starts, seg[E] = total
   int* wcnt = seg + E + 1;         // [4][E]
-  int* tmp = wcnt + 4 * E;         // [16]
-  for (int x = threadIdx.x; x < nc * E; x += blockDim.x) counts[x] = a.chunk_counts[x];
+  int* tmp = wcnt + 4 * E;         // [17]
+  const int64_t begin = (int64_t)b * a.chunk;
+  const int64_t end = min(a.n, begin + a.chunk);
+  // The chunk's first kIdBatch rounds of entries load first, in flight while
+  // the count table is staged and scanned; the table loads go out
+  // kStageBatch at a time (one dependent load per iteration would cost a
+  // memory latency per kAlignThreads ints).
+  int ev[kIdBatch];
+#pragma unroll
+  for (int u = 0; u < kIdBatch; ++u)
+    ev[u] = local_expert(a.topk_ids, begin + (int64_t)u * blockDim.x + threadIdx.x, end,
+                         a.expert_begin, E);
+  for (int x0 = threadIdx.x; x0 < nc * E; x0 += blockDim.x * kStageBatch) {
+    int v[kStageBatch];
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u) {
+      const int x = x0 + u * (int)blockDim.x;
+      v[u] = x < nc * E ? a.chunk_counts[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u) {
+      const int x = x0 + u * (int)blockDim.x;
+      if (x < nc * E) counts[x] = v[u];
+    }
+  }
   for (int x = threadIdx.x; x < 4 * E; x += blockDim.x) wcnt[x] = 0;
   __syncthreads();
   // Thread t owns experts [t*per, t*per + per): count over all chunks, count
@@ -222,11 +241,20 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter(AlignArgs a) {
   const int64_t all_blocks = (a.max_padded + bm - 1) / bm;
   for (int64_t blk = used_blocks + gt; blk < all_blocks; blk += gs) a.expert_ids[blk] = -1;
   for (int64_t p = total + gt; p < a.max_padded; p += gs) a.sorted_ids[p] = sentinel;
-  const int64_t begin = (int64_t)b * a.chunk;
-  const int64_t end = min(a.n, begin + a.chunk);
-  for (int64_t base = begin; base < end; base += blockDim.x)
-    scatter_round(a.topk_ids, base + threadIdx.x, end, a.expert_begin, E, running, wcnt,
-                  a.sorted_ids);
+  for (int64_t base0 = begin; base0 < end; base0 += (int64_t)blockDim.x * kIdBatch) {
+    if (base0 != begin) {  // later batches (chunks above kIdBatch rounds)
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u)
+        ev[u] = local_expert(a.topk_ids, base0 + (int64_t)u * blockDim.x + threadIdx.x, end,
+                             a.expert_begin, E);
+    }
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int64_t base = base0 + (int64_t)u * blockDim.x;
+      if (base >= end) break;  // uniform
+      scatter_round(ev[u], base + threadIdx.x, E, running, wcnt, a.sorted_ids);
+    }
+  }
 }
 
 }  // namespace
@@ -234,7 +262,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter(AlignArgs a) {
 hipError_t launch_align(const AlignArgs& a, hipStream_t stream) {
   const int E = a.num_experts;
   if (align_single_workgroup(a.n, E)) {
-    const size_t lds = (size_t)(17 * E + 16) * sizeof(int);
+    const size_t lds = (size_t)(17 * E + 17) * sizeof(int);
     hipLaunchKernelGGL(align_single, dim3(1), dim3(1024), lds, stream, a);
     return hipGetLastError();
   }
@@ -242,7 +270,7 @@ hipError_t launch_align(const AlignArgs& a, hipStream_t stream) {
                      stream, a);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds = ((size_t)a.nchunks * E + 6 * (size_t)E + 17) * sizeof(int);
+  const size_t lds = ((size_t)a.nchunks * E + 6 * (size_t)E + 18) * sizeof(int);
   hipLaunchKernelGGL(align_scatter, dim3(a.nchunks), dim3(kAlignThreads), lds, stream, a);
   return hipGetLastError();
 }

@@ -34,62 +34,63 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return r;
 }
 
-// Exclusive scan of one int per thread across the workgroup (blockDim.x a
-// multiple of 64, at most 1024).  `tmp` holds >= 16 ints of LDS.
-__device__ inline int block_scan_excl(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  int base = 0, sum = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int t = tmp[w];
-    if (w < wave) base += t;
-    sum += t;
-  }
-  __syncthreads();
-  *total = sum;
-  return base + x - v;
+// Inclusive scan over the 64 lanes of a wave in registers (DPP, no LDS):
+// rows of 16 lanes add their left neighbours 1, 2, 4 and 8 places away
+// (lanes without one in the row add 0), then rows 1 and 3 add the last lane
+// of the row before, and rows 2 and 3 the last lane of row 1.  The first
+// four steps alone scan each row of 16.
+__device__ __forceinline__ int row_incl_scan16(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = row_incl_scan16(x);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
 }
 
-// Exclusive scans of N ints per thread across the workgroup at once (same
-// contract as block_scan_excl; `tmp` holds >= 16 * N ints of LDS): v[i]
-// becomes the exclusive prefix of counter i, total[i] its sum.  Two barriers
-// for all N counters instead of two per counter.
+// Exclusive scans of N ints per thread across the workgroup (blockDim.x a
+// multiple of 64, at most 1024; `tmp` holds >= 17 * N ints of LDS): v[i]
+// becomes the exclusive prefix of counter i over the thread order, total[i]
+// its sum.  Each wave scans its lanes in registers; wave 0 then scans the
+// (at most 16) wave totals the same way and writes back each wave's
+// inclusive prefix and the totals, so every thread reads 2N values from LDS
+// in one batch (a loop over the wave totals in every thread would wait for
+// one LDS read at a time).  Three barriers for all N counters.
 template <int N>
 __device__ inline void block_scan_excl_n(int (&v)[N], int* tmp, int (&total)[N]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int x[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) x[i] = v[i];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int y = __shfl_up(x[i], d, 64);
-      if (lane >= d) x[i] += y;
-    }
-  }
+  for (int i = 0; i < N; ++i) x[i] = wave_incl_scan(v[i]);
   if (lane == 63) {
 #pragma unroll
     for (int i = 0; i < N; ++i) tmp[wave * N + i] = x[i];
   }
   __syncthreads();
+  if (wave == 0) {
+    int s[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) s[i] = row_incl_scan16(lane < nw ? tmp[lane * N + i] : 0);
+    if (lane < nw) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) tmp[lane * N + i] = s[i];
+    }
+    if (lane == nw - 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) tmp[16 * N + i] = s[i];
+    }
+  }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    int base = 0, sum = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int t = tmp[w * N + i];
-      if (w < wave) base += t;
-      sum += t;
-    }
-    v[i] = base + x[i] - v[i];
-    total[i] = sum;
+    const int before = wave > 0 ? tmp[(wave - 1) * N + i] : 0;
+    total[i] = tmp[16 * N + i];
+    v[i] = before + x[i] - v[i];
   }
   __syncthreads();
 }

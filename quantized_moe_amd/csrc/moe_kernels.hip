@@ -20,7 +20,7 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
   __shared__ int first[kMaxExperts];
   __shared__ int last[kMaxExperts];
   __shared__ int nblk[kMaxExperts];
-  __shared__ int scan_tmp[16 * 11];
+  __shared__ int scan_tmp[17 * 11];
   __shared__ int err;
   const int tid = threadIdx.x;
   const int E = a.num_experts;
@@ -42,19 +42,40 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
       ntpp = ntpp < 0 ? 0 : (ntpp > a.max_padded ? a.max_padded : ntpp);
     }
     const int64_t nb = min(ntpp / a.block_m, nb_cap);
-    for (int64_t b = tid; b < nb; b += blockDim.x) {
-      const int e = a.expert_ids[b];
-      if (e < 0 || e >= E) {
-        if (a.validate) atomicOr(&err, 1);
-        continue;
+    // Extents from run boundaries: a block whose left (right) neighbour
+    // belongs to another expert starts (ends) a run of its expert.  Only the
+    // boundaries touch the LDS tables (a wave of same-expert blocks would
+    // otherwise serialise 64 atomics on one address), nblk counts the runs
+    // (one per expert in a valid layout), and each thread keeps the ids of
+    // kBatch blocks and their neighbours in flight together.
+    constexpr int kBatch = 4;
+    for (int64_t b0 = tid; b0 < nb; b0 += (int64_t)blockDim.x * kBatch) {
+      int ec[kBatch], ep[kBatch], en[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t b = b0 + (int64_t)u * blockDim.x;
+        ec[u] = b < nb ? a.expert_ids[b] : -1;
+        ep[u] = (b < nb && b > 0) ? a.expert_ids[b - 1] : INT32_MIN;
+        en[u] = b + 1 < nb ? a.expert_ids[b + 1] : INT32_MIN;
       }
-      atomicMin(&first[e], (int)b);
-      atomicMax(&last[e], (int)b);
-      atomicAdd(&nblk[e], 1);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t b = b0 + (int64_t)u * blockDim.x;
+        if (b >= nb) break;
+        const int e = ec[u];
+        if (e < 0 || e >= E) {
+          if (a.validate) atomicOr(&err, 1);
+          continue;
+        }
+        if (ep[u] != e) {
+          atomicMin(&first[e], (int)b);
+          atomicAdd(&nblk[e], 1);
+        }
+        if (en[u] != e) atomicMax(&last[e], (int)b);
+      }
     }
     __syncthreads();
-    if (tid < E && last[tid] >= 0 && a.validate && last[tid] - first[tid] + 1 != nblk[tid])
-      atomicOr(&err, 2);
+    if (tid < E && last[tid] >= 0 && a.validate && nblk[tid] != 1) atomicOr(&err, 2);
   } else if (a.layout == kMasked) {
     if (tid < E) {
       int m = a.masked_m[tid];
