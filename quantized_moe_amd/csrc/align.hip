@@ -197,11 +197,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter(AlignArgs a) {
   for (int q = 0; q < per; ++q) {
     const int e = e0 + q;
     if (e >= E) break;
+    // Eight independent LDS reads per step (a plain loop waits for each).
     int tot = 0, before = 0;
-    for (int c = 0; c < nc; ++c) {
-      const int v = counts[c * E + e];
-      before += c < b ? v : 0;
-      tot += v;
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? counts[(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        before += c0 + u < b ? v[u] : 0;
+        tot += v[u];
+      }
     }
     running[e] = before;
     seg[e] = tot;

@@ -47,16 +47,18 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
     // boundaries touch the LDS tables (a wave of same-expert blocks would
     // otherwise serialise 64 atomics on one address), nblk counts the runs
     // (one per expert in a valid layout), and each thread keeps the ids of
-    // kBatch blocks and their neighbours in flight together.
+    // kBatch blocks and their neighbours in flight together.  The first batch
+    // is read before the padded total is known (inside the buffer's nb_cap
+    // blocks), so its loads overlap the load of the total.
     constexpr int kBatch = 4;
-    for (int64_t b0 = tid; b0 < nb; b0 += (int64_t)blockDim.x * kBatch) {
+    for (int64_t b0 = tid; b0 == tid || b0 < nb; b0 += (int64_t)blockDim.x * kBatch) {
       int ec[kBatch], ep[kBatch], en[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int64_t b = b0 + (int64_t)u * blockDim.x;
-        ec[u] = b < nb ? a.expert_ids[b] : -1;
-        ep[u] = (b < nb && b > 0) ? a.expert_ids[b - 1] : INT32_MIN;
-        en[u] = b + 1 < nb ? a.expert_ids[b + 1] : INT32_MIN;
+        ec[u] = b < nb_cap ? a.expert_ids[b] : -1;
+        ep[u] = (b < nb_cap && b > 0) ? a.expert_ids[b - 1] : INT32_MIN;
+        en[u] = b + 1 < nb_cap ? a.expert_ids[b + 1] : INT32_MIN;
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -67,11 +69,11 @@ __global__ __launch_bounds__(1024) void build_tiles(TileBuildArgs a) {
           if (a.validate) atomicOr(&err, 1);
           continue;
         }
-        if (ep[u] != e) {
+        if (b == 0 || ep[u] != e) {
           atomicMin(&first[e], (int)b);
           atomicAdd(&nblk[e], 1);
         }
-        if (en[u] != e) atomicMax(&last[e], (int)b);
+        if (b + 1 >= nb || en[u] != e) atomicMax(&last[e], (int)b);
       }
     }
     __syncthreads();
