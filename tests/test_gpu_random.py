@@ -57,3 +57,45 @@ def test_indexed_random_shapes(seed):
     assert int(ntpp[0]) == int(ref_ntpp)
     assert np.array_equal(sorted_ids, ref_sorted)
     assert np.array_equal(expert_ids, ref_experts)
+
+
+def draw_masked_case(seed):
+    rng = np.random.Generator(np.random.PCG64(5000 + seed))
+    E = int(rng.integers(1, 25))
+    max_m = int(rng.choice([16, 40, 64, 200, 256]))
+    H = int(rng.choice([128, 384, 512, 768]))
+    I = int(rng.choice([128, 256, 384, 512]))
+    pattern = int(rng.integers(0, 3))  # 0: uniform, 1: one hot expert, 2: empty and full experts
+    if pattern == 0:
+        mm = rng.integers(0, max_m + 1, E)
+    elif pattern == 1:
+        mm = rng.integers(0, max(2, max_m // 8), E)
+        mm[int(rng.integers(0, E))] = max_m
+    else:
+        mm = rng.choice([0, max_m, int(rng.integers(1, max_m + 1))], E)
+    expected_m = int(rng.integers(1, max_m + 1))
+    return dict(E=E, max_m=max_m, H=H, I=I, mm=mm.astype(np.int32), expected_m=expected_m,
+                pattern=pattern)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_masked_random_shapes(seed):
+    from quantized_moe_amd import chord as C
+    from quantized_moe_amd.moe import W4A16MoE
+    from moe_inputs import gen as G
+    from tests.gpu_util import dev, dev_bf16, host_bf16
+    c = draw_masked_case(seed)
+    banner(f"random masked case {seed}: E={c['E']} max_m={c['max_m']} H={c['H']} I={c['I']} "
+           f"pattern={c['pattern']} expected_m={c['expected_m']} masked_m={c['mm'].tolist()}")
+    rng = np.random.Generator(np.random.PCG64(7000 + seed))
+    E, max_m, H, I, mm = c["E"], c["max_m"], c["H"], c["I"], c["mm"]
+    a3 = G.draw_activations(rng, E * max_m, H).reshape(E, max_m, H)
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H, scale_mult=(256.0 / H) ** 0.5)
+    q2, s2 = G.draw_weights(rng, E, H, I, scale_mult=(256.0 / I) ** 0.5)
+    layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2), mode=C.MODE_MASKED)
+    got = host_bf16(layer.masked(dev_bf16(a3), dev(mm), c["expected_m"]))
+    ref = oracle.grouped_masked(a3, mm, q13, s13, q2, s2)
+    valid = np.zeros(E * max_m, bool)
+    for e in range(E):
+        valid[e * max_m:e * max_m + int(mm[e])] = True
+    check_close(got[valid], ref[valid], what=f"random masked case {seed}")
