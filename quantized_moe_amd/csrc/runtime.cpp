@@ -292,6 +292,13 @@ Plan make_plan(const PlanKey& key) {
     if (wk == 1 || wk == 2 || wk == 4) g.wk = wk;
     if (ov_pf == 2 || ov_pf == 4) g.pf = ov_pf;
     if ((N / 16) % g.nt != 0) g.nt = 2;
+    // A handful of routed rows on a deep-K GEMM (the TP slice at T = 1): the
+    // 4-way split leaves half the CUs idle and each wave a serial chain of 14
+    // chunk loads, so K splits over 8 waves (2 weight tiles, one token tile;
+    // not selectable by overrides).
+    if (nt == 0 && wk == 0 && g.nt == 2 && mt == 1 && chunks >= 32 &&
+        tiles_guess * (N / 16 / 2) <= key.cus / 2)
+      g.wk = 8;
     // Short K (<= 2 chunks): an item covers several groups of weight tiles of
     // one token tile (token fragments loaded once, weight loads pipelined
     // across the groups), about 8 items per CU of expected tiles.
