@@ -27,6 +27,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// SiLU(g) * u in fp32 for the fused gate_up epilogue: g * rcp(1 + e^-g) * u
+// with the hardware exp and reciprocal (each within about 1 ulp; the result
+// is rounded to bf16 next).  g -> -inf gives -0, g -> +inf gives g, NaN
+// propagates.  Every kernel family uses this one definition, so they agree
+// bit for bit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // (a & m) | c in one VALU instruction (the compiler otherwise emits two).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   uint32_t r;

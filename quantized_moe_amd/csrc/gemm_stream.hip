@@ -77,10 +77,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
-}
-
 // Row mapping of one tile row: the B source row and the output row, or -1.
 struct RowMap {
   int64_t src;

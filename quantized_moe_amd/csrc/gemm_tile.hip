@@ -68,10 +68,6 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int st) {
   return st == 0 ? v.x : st == 1 ? v.y : st == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
-}
-
 struct RowMap {
   int64_t src;
   int64_t dst;
