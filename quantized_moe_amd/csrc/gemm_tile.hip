@@ -95,7 +95,7 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
 
 // Down epilogue: y = acc * row weight, bf16.  Lane (q, col) holds outputs
 // 4q .. 4q+3 of each weight tile for token col; lanes exchange packed halves
-// (cross-lane reads) so that each lane stores 16 contiguous bytes: lane q
+// (two register row swaps) so that each lane stores 16 contiguous bytes: lane q
 // takes tile 2i + q / 2, outputs 8 (q % 2) .. 8 (q % 2) + 7, from lanes
 // 2 (q % 2) and 2 (q % 2) + 1 of its token.  Stores of 16 instead of 8 bytes
 // per lane (32 -> 64 contiguous bytes per token row) made the short-K down
@@ -105,7 +105,6 @@ __device__ __forceinline__ void store_down_pairs(const GemmArgs& a, const f32x4_
                                                  const int64_t* dstrow, const float* roww,
                                                  int tile0, int q, int col) {
   static_assert(NT % 2 == 0, "tile pairs");
-  const int src0 = ((2 * q) & 3) * 16 + col, src1 = src0 + 16;
 #pragma unroll
   for (int g = 0; g < MG; ++g) {
     const int64_t dr = dstrow[g * 16 + col];
@@ -115,15 +114,19 @@ __device__ __forceinline__ void store_down_pairs(const GemmArgs& a, const f32x4_
       const f32x4_t v0 = acc[2 * i][g], v1 = acc[2 * i + 1][g];
       const uint32_t p0x = pk_bf16(v0[0] * rw, v0[1] * rw), p0y = pk_bf16(v0[2] * rw, v0[3] * rw);
       const uint32_t p1x = pk_bf16(v1[0] * rw, v1[1] * rw), p1y = pk_bf16(v1[2] * rw, v1[3] * rw);
-      const uint32_t a0 = __shfl(p0x, src0), a1 = __shfl(p0y, src0);
-      const uint32_t a2 = __shfl(p0x, src1), a3 = __shfl(p0y, src1);
-      const uint32_t b0 = __shfl(p1x, src0), b1 = __shfl(p1y, src0);
-      const uint32_t b2 = __shfl(p1x, src1), b3 = __shfl(p1y, src1);
+      // Row exchange in registers: swapping the upper two 16-lane rows of the
+      // tile-2i values with the lower two of the tile-2i+1 values, then odd
+      // with even rows, leaves lane (q, col) with rows (2q & 3) and its
+      // successor of tile 2i + q / 2: its 16 contiguous output bytes.
+      const auto sx = __builtin_amdgcn_permlane32_swap(p0x, p1x, false, false);
+      const auto sy = __builtin_amdgcn_permlane32_swap(p0y, p1y, false, false);
+      const auto tx = __builtin_amdgcn_permlane16_swap(sx[0], sx[1], false, false);
+      const auto ty = __builtin_amdgcn_permlane16_swap(sy[0], sy[1], false, false);
       if (dr < 0) continue;
       const int tw = tile0 + 2 * i + (q >> 1);
       const int n0 = tw * 16 + (q & 1) * 8;
       *reinterpret_cast<uint4*>(a.out + dr * (int64_t)a.out_ld + n0) =
-          q < 2 ? make_uint4(a0, a1, a2, a3) : make_uint4(b0, b1, b2, b3);
+          make_uint4(tx[0], ty[0], tx[1], ty[1]);
     }
   }
 }
