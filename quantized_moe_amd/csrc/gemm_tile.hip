@@ -206,6 +206,27 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
     }
   };
 
+  // Load piece j of chunk c into buffer `slot`: pieces 0 .. kDma-1 are the
+  // token DMA instructions, then per weight tile the codes and the scale,
+  // i.e. the order load_x followed by load_w issues them.
+  constexpr int kPieces = kDma + 2 * NT;
+  auto load_piece = [&](int j, int slot, int c) {
+    if (j < kDma) {
+      uint8_t* dst = xbuf + slot * kXBufBytes + jblk[j] * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void*)dst, 16, voff[j], c * kChunkK * 2, 0, 0);
+      return;
+    }
+    const int nt = (j - kDma) >> 1;
+    const uint32_t blk = (uint32_t)((tile_ld + nt) * nc + c) * kBlockBytes;
+    if (((j - kDma) & 1) == 0) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+      wq[slot][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+      sc[slot][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+    }
+  };
+
   f32x4_t acc[NT][MG];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -230,7 +251,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   auto bread = [&](const uint8_t* xb, int st, int g) {
     return *reinterpret_cast<const bf16x8_t*>(xb + boff[st] + g * 16 * 256);
   };
-  auto compute = [&](int slot, int next) {
+  auto compute = [&](int slot, int next, int fill, int cfill) {
     const uint8_t* xb = xbuf + slot * kXBufBytes;
     DqScale ks[NT];
 #pragma unroll
@@ -257,6 +278,12 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
           an[nt] = st < 3 ? dequant_word(word_of(wq[slot][nt], st + 1), ks[nt])
                           : dequant_word(wq[next][nt].x, dq_scale(sc[next][nt]));
         }
+        // Prefetch pieces of chunk cfill, spread evenly over all but the last
+        // two sections (spread over all of them, the 11-group variant
+        // spills registers).
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j)
+          if (j * (4 * MG - 2) / kPieces == idx) load_piece(j, fill, cfill);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -264,8 +291,11 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
     }
   };
 
-  // Chunk c in buffer c % 3: x(c+2) DMA and weights(c+2) loads into the
-  // buffer freed by chunk c-1, compute(c), then wait until the DMA of x(c+1)
+  // Chunk c in buffer c % 3: compute(c), issuing the x(c+2) DMA and the
+  // weights(c+2) loads into the buffer freed by chunk c-1 one piece at a
+  // time between its group sections (issued together at the chunk start,
+  // the 8 waves' ~66 KB per CU queued behind each other at the texture unit
+  // for ~0.4 us with no math in between), then wait until the DMA of x(c+1)
   // (issued one chunk ago) has landed and pass the workgroup barrier.  The
   // barrier is a bare s_barrier with an explicit vmcnt wait: a fenced
   // __syncthreads would also wait for the x(c+2) DMA just issued.  Loads
@@ -279,10 +309,7 @@ __device__ __forceinline__ void run_item(const GemmArgs& a, uint8_t* xbuf, const
   auto chunk = [&](int slot, int c) {
     const int c2 = c + 2 < c_hi ? c + 2 : c_hi - 1;
     const int fill = slot == 0 ? 2 : slot - 1;
-    load_x(fill, c2);
-    load_w(fill, c2);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-    compute(slot, slot == 2 ? 0 : slot + 1);
+    compute(slot, slot == 2 ? 0 : slot + 1, fill, c2);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitX);
     __builtin_amdgcn_s_barrier();
