@@ -131,6 +131,21 @@ const char* chord_last_error(void);
  * CHORD_ERR_INVALID_ARGUMENT if buf is NULL or n == 0. */
 chord_status chord_last_plan(char* buf, size_t n);
 
+/* The schedule a layer call would choose, computed on the host alone: no GPU,
+ * no HIP call.  Describes a call by its mode (CHORD_MODE_*), T and k (indexed
+ * and contiguous; ignored for masked), the global expert count (indexed), the
+ * local expert count E_l, H, I, a size hint (indexed: block_m; contiguous:
+ * valid_m_hint; masked: expected_m), its internal rows (indexed: max_padded;
+ * contiguous: M; masked: E_l * max_m) and the compute units to plan for
+ * (0: the MI355X's 256).  An override (indexed only, may be NULL) is applied
+ * as the layer call applies it.  Writes "<mode>: <plan>" in the format of
+ * chord_last_plan into buf[0..n).  Returns CHORD_OK or
+ * CHORD_ERR_INVALID_ARGUMENT (bad descriptor, override out of range, NULL
+ * buf or n == 0). */
+chord_status chord_w4a16_moe_plan(int mode, int T, int k, int num_global_experts, int E_l, int H,
+                                  int I, int hint, int64_t rows, int num_cus,
+                                  const chord_schedule* override, char* buf, size_t n);
+
 /* Library version string. */
 const char* chord_version(void);
 

@@ -32,6 +32,7 @@ EXPORTED = [
     "chord_w4a16_moe_grouped_contiguous", "chord_w4a16_moe_grouped_masked",
     "chord_moe_dispatch_contiguous_rows", "chord_moe_dispatch_workspace_bytes",
     "chord_moe_dispatch_contiguous", "chord_moe_dispatch_masked", "chord_moe_combine",
+    "chord_w4a16_moe_plan",
 ]
 
 
@@ -88,6 +89,8 @@ def _load():
         "chord_moe_dispatch_contiguous": (I, [P, I, I, P, I, I, I, P, P, I64, P, P, P, SZ, P]),
         "chord_moe_dispatch_masked": (I, [P, I, I, P, I, I, I, I, P, P, P, P, P, SZ, P]),
         "chord_moe_combine": (I, [P, I64, I, P, P, I, I, P, P]),
+        "chord_w4a16_moe_plan": (I, [I, I, I, I, I, I, I, I, I64, I, ctypes.POINTER(Schedule),
+                                     ctypes.c_char_p, SZ]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -215,6 +218,15 @@ def _sched(override):
     for name, _ in Schedule._fields_:
         setattr(s, name, int(override.get(name, 0)))
     return ctypes.byref(s)
+
+
+def chord_w4a16_moe_plan(mode, T, k, num_global_experts, E_l, H, I, hint, rows, num_cus=0,
+                         override=None) -> str:
+    """The schedule a layer call with this descriptor would choose (host only)."""
+    buf = ctypes.create_string_buffer(512)
+    _check(lib.chord_w4a16_moe_plan(mode, T, k, num_global_experts, E_l, H, I, hint, rows,
+                                    num_cus, _sched(override), buf, 512))
+    return buf.value.decode()
 
 
 def chord_w4a16_moe_indexed(x, w13: PackedWeight, w2: PackedWeight, topk_ids, topk_weights,

@@ -716,6 +716,20 @@ chord_status dispatch_prepare(const chord_bf16* x, int T, int H, const int32_t* 
   return CHORD_OK;
 }
 
+// Every field of a schedule override within the values the kernels are
+// instantiated for (0 = automatic).
+bool override_in_range(const chord_schedule* o) {
+  auto in = [](int v, std::initializer_list<int> ok) {
+    for (int x : ok)
+      if (v == x) return true;
+    return false;
+  };
+  return in(o->kernel, {0, 1, 2, 3}) && in(o->tokens, {0, 16, 32}) &&
+         in(o->gate_up_nt, {0, 2, 4}) && in(o->down_nt, {0, 2, 4}) &&
+         in(o->gate_up_wk, {0, 1, 2, 4}) && in(o->down_wk, {0, 1, 2, 4}) &&
+         in(o->prefetch, {0, 2, 4}) && in(o->tile_split, {0, 1});
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -741,6 +755,31 @@ const char* chord_last_error(void) { return g_last_error.c_str(); }
 chord_status chord_last_plan(char* buf, size_t n) {
   if (!buf || n == 0) return CHORD_ERR_INVALID_ARGUMENT;
   snprintf(buf, n, "%s", g_last_plan.c_str());
+  return CHORD_OK;
+}
+
+chord_status chord_w4a16_moe_plan(int mode, int T, int k, int num_global_experts, int E_l, int H,
+                                  int I, int hint, int64_t rows, int num_cus,
+                                  const chord_schedule* override, char* buf, size_t n) {
+  if (!buf || n == 0) return fail(CHORD_ERR_INVALID_ARGUMENT, "null or empty output buffer");
+  if (mode != kIndexed && mode != kContiguous && mode != kMasked)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "mode %d", mode);
+  if (E_l < 1 || E_l > kMaxExperts || H <= 0 || I <= 0 || H % kChunkK != 0 || I % kChunkK != 0 ||
+      rows < 0 || num_cus < 0 || hint < 0 || T < 0 || k < 0 || num_global_experts < 0)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "bad call descriptor");
+  if (mode == kIndexed && (T < 1 || k < 1 || !valid_bm(hint)))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "indexed plans need T, k and a block_m of 16..128");
+  if (mode != kIndexed && override)
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "grouped calls take no schedule override");
+  if (override && !override_in_range(override))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
+  PlanKey key{mode, mode == kMasked ? 0 : T, mode == kMasked ? 0 : k,
+              mode == kIndexed ? num_global_experts : 0, E_l, H, I, hint,
+              num_cus > 0 ? num_cus : 256, {0}, rows};
+  fill_override(key, override);
+  const Plan plan = get_plan(key);
+  snprintf(buf, n, "%s: %s", mode == kIndexed ? "indexed" : mode == kContiguous ? "contiguous" : "masked",
+           plan.text);
   return CHORD_OK;
 }
 
@@ -1023,18 +1062,8 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
     return fail(CHORD_ERR_UNSUPPORTED, "routing tensors too large");
   if ((int64_t)T * k * H * 2 > INT32_MAX)  // y rows are read through a 32-bit buffer offset
     return fail(CHORD_ERR_UNSUPPORTED, "T*k*H*2 exceeds 2 GiB");
-  if (override) {
-    auto in = [](int v, std::initializer_list<int> ok) {
-      for (int o : ok)
-        if (v == o) return true;
-      return false;
-    };
-    if (!in(override->kernel, {0, 1, 2, 3}) || !in(override->tokens, {0, 16, 32}) ||
-        !in(override->gate_up_nt, {0, 2, 4}) || !in(override->down_nt, {0, 2, 4}) ||
-        !in(override->gate_up_wk, {0, 1, 2, 4}) || !in(override->down_wk, {0, 1, 2, 4}) ||
-        !in(override->prefetch, {0, 2, 4}) || !in(override->tile_split, {0, 1}))
-      return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
-  }
+  if (override && !override_in_range(override))
+    return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
   const WsLayout ws = layer_ws(kIndexed, T, k, E_l, H, I, max_padded);
   if (!workspace || ws_bytes < ws.total)
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);

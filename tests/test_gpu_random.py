@@ -57,6 +57,13 @@ def test_indexed_random_shapes(seed):
     assert int(ntpp[0]) == int(ref_ntpp)
     assert np.array_equal(sorted_ids, ref_sorted)
     assert np.array_equal(expert_ids, ref_experts)
+    # The host-only planner query names the schedule the call took.
+    import torch
+    C = parity.C
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert C.last_plan() == C.chord_w4a16_moe_plan(
+        C.MODE_INDEXED, c["T"], c["k"], c["E_g"], c["E_l"], c["H"], c["I"], c["bm"],
+        sorted_ids.shape[0], num_cus=cus, override=override)
 
 
 def draw_masked_case(seed):

@@ -1,0 +1,92 @@
+"""CPU tests of the planner through the host-only query entry point: the
+schedule each benchmark-shaped call would get, the effect of overrides and of
+the compute-unit count, and the query's own argument checks.  No GPU: the
+query makes no HIP call."""
+
+import ctypes
+
+import pytest
+
+from quantized_moe_amd import chord as C
+
+
+def indexed(T, k, E_g, E_l, H, I, **kw):
+    bm = C.chord_w4a16_moe_indexed_block_m(T, k, E_g, E_l, H, I)
+    mp = C.chord_moe_align_max_padded(T, k, E_l, bm)
+    return C.chord_w4a16_moe_plan(C.MODE_INDEXED, T, k, E_g, E_l, H, I, bm, mp, **kw)
+
+
+def test_decode_streams_weights_with_split_k_gate_up():
+    # 64 tokens over 48 of 384 experts: about one token per expert, so every
+    # GEMM streams its weights once; gate_up splits K over two waves.
+    p = indexed(64, 8, 384, 48, 7168, 2048)
+    assert p.startswith("indexed: ") and "| stream " in p
+    assert "gate_up nt=2 wk=2" in p and "down nt=4 wk=1" in p
+
+
+def test_prefill_and_large_tp_slices_take_the_tiled_kernel():
+    assert "| tile 256x192" in indexed(8192, 8, 384, 48, 7168, 2048)
+    for T in (512, 4096):
+        assert "| tile 256x192" in indexed(T, 8, 384, 384, 7168, 256), T
+
+
+def test_single_token_tp_slice_splits_gate_up_eight_ways():
+    # I = 256: two K chunks per down row and a short gate_up; with so few
+    # tiles the gate_up K split goes to eight waves to fill the chip.
+    p = indexed(1, 8, 384, 384, 7168, 256)
+    assert "| stream " in p and "gate_up nt=2 wk=8" in p
+
+
+def test_small_tp_slice_streams():
+    assert "| stream " in indexed(32, 8, 384, 384, 7168, 256)
+
+
+def test_grouped_layouts_plan_the_tiled_kernel():
+    M = 8192 * 8 * 48 // 384
+    p = C.chord_w4a16_moe_plan(C.MODE_CONTIGUOUS, 8192, 8, 0, 48, 7168, 2048, M, M + 48 * 128)
+    assert p.startswith("contiguous: ") and "| tile 256x192" in p
+    for E in (24, 48, 96):
+        p = C.chord_w4a16_moe_plan(C.MODE_MASKED, 0, 0, 0, E, 7168, 2048, 100, E * 256)
+        assert p.startswith("masked: ") and "| tile 256x192" in p, E
+
+
+def test_overrides_select_the_kernel_family():
+    assert "| tile " in indexed(64, 8, 384, 48, 7168, 2048, override={"kernel": 2})
+    assert "| stream " in indexed(8192, 8, 384, 48, 7168, 2048, override={"kernel": 1})
+    p = indexed(64, 8, 384, 48, 7168, 2048, override={"gate_up_wk": 4, "down_nt": 2})
+    assert "gate_up nt=2 wk=4" in p and "down nt=2" in p
+
+
+def test_plans_are_deterministic_and_accept_other_cu_counts():
+    a = indexed(64, 8, 384, 48, 7168, 2048)
+    assert indexed(64, 8, 384, 48, 7168, 2048) == a
+    assert indexed(64, 8, 384, 48, 7168, 2048, num_cus=256) == a
+    for cus in (1, 80, 304):
+        assert indexed(64, 8, 384, 48, 7168, 2048, num_cus=cus).startswith("indexed: ")
+
+
+@pytest.mark.parametrize("args, override", [
+    ((3, 64, 8, 384, 48, 7168, 2048, 16, 1024), None),                 # mode
+    ((0, 64, 8, 384, 48, 7100, 2048, 16, 1024), None),                 # H % 128
+    ((0, 64, 8, 384, 48, 7168, 2048, 24, 1024), None),                 # block_m
+    ((0, 0, 8, 384, 48, 7168, 2048, 16, 1024), None),                  # T
+    ((0, 64, 8, 384, 0, 7168, 2048, 16, 1024), None),                  # E_l
+    ((0, 64, 8, 384, 48, 7168, 2048, 16, -1), None),                   # rows
+    ((2, 0, 0, 0, 48, 7168, 2048, 100, 48 * 256), {"kernel": 1}),      # grouped override
+    ((0, 64, 8, 384, 48, 7168, 2048, 16, 1024), {"gate_up_wk": 3}),    # out of range
+])
+def test_query_rejects_bad_descriptors(args, override):
+    with pytest.raises(C.ChordError) as e:
+        C.chord_w4a16_moe_plan(*args, override=override)
+    assert e.value.status == 1
+
+
+def test_query_rejects_null_buffer():
+    st = C.lib.chord_w4a16_moe_plan(0, 64, 8, 384, 48, 7168, 2048, 16, 1024, 0, None, None, 16)
+    assert st == 1
+    buf = ctypes.create_string_buffer(8)
+    st = C.lib.chord_w4a16_moe_plan(0, 64, 8, 384, 48, 7168, 2048, 16, 1024, 0, None, buf, 0)
+    assert st == 1
+    # A short buffer is filled and terminated, not overrun.
+    assert C.lib.chord_w4a16_moe_plan(0, 64, 8, 384, 48, 7168, 2048, 16, 1024, 0, None, buf, 8) == 0
+    assert buf.value == b"indexed"
