@@ -495,6 +495,7 @@ hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArg
 #define CHORD_STREAM_MT(NT, MT) \
   CHORD_STREAM_WK(NT, MT, 1) CHORD_STREAM_WK(NT, MT, 2) CHORD_STREAM_WK(NT, MT, 4)
     CHORD_STREAM_MT(2, 1)
+    CHORD_STREAM_CASE(1, 1, 8, 4)
     CHORD_STREAM_WK(2, 1, 8)
     CHORD_STREAM_MT(2, 2)
     CHORD_STREAM_MT(4, 1)

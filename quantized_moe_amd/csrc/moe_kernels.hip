@@ -313,16 +313,18 @@ __global__ void clear_status(DevStatus* s) {
 // uniform across the wave, so the slot ids (or the slot -> row map) and the
 // weights are scalar loads and the per-batch branch is uniform.  Each lane
 // owns kCombinePieces 16-byte pieces (8 outputs each), and the row loads of
-// kCombineBatch slots are issued together.  Batches of 2 skip more empty
-// slots on sparse routing (one local slot of 8 on the prefill share: 48 ->
-// 45 us) and cost nothing measurable when every slot is local (TP slice).
+// B slots are issued together.  Batches of 2 skip more empty slots on sparse
+// routing (one local slot of 8 on the prefill share: 48 -> 45 us) and cost
+// nothing measurable when every slot is local (TP slice).  With fewer waves
+// than SIMDs the kernel is a chain of memory latencies, so all 8 slots of a
+// top-8 token go out in one batch.  B does not change the summation order.
 // ---------------------------------------------------------------------------
 constexpr int kCombineWaves = 4;
 constexpr int kCombinePieces = 2;
-constexpr int kCombineBatch = 2;
 
+template <int B>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
-  constexpr int P = kCombinePieces, B = kCombineBatch;
+  constexpr int P = kCombinePieces;
   const int nvec = a.H / 8;
   const int spans = (nvec + 64 * P - 1) / (64 * P);
   // T * spans < 2^31 (host-checked), so 32-bit wave indexing; every value
@@ -433,8 +435,11 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const int per_wave = 64 * kCombinePieces;
   const int64_t waves = (int64_t)a.T * ((a.H / 8 + per_wave - 1) / per_wave);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((waves + kCombineWaves - 1) / kCombineWaves)),
-                     dim3(64 * kCombineWaves), 0, stream, a);
+  const dim3 grid((unsigned)((waves + kCombineWaves - 1) / kCombineWaves));
+  if (waves < 1024)
+    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(64 * kCombineWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(64 * kCombineWaves), 0, stream, a);
   return hipGetLastError();
 }
 

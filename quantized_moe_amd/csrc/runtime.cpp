@@ -299,6 +299,13 @@ Plan make_plan(const PlanKey& key) {
     if (nt == 0 && wk == 0 && g.nt == 2 && mt == 1 && chunks >= 32 &&
         tiles_guess * (N / 16 / 2) <= key.cus / 2)
       g.wk = 8;
+    // Still no more single-tile items than CUs: one weight tile per item, so
+    // every CU holds a workgroup, and 4 chunks in flight per wave (T = 1
+    // gate_up: 11.9 -> 10.3 us).
+    if (g.wk == 8 && tiles_guess * (N / 16) <= key.cus) {
+      g.nt = 1;
+      g.pf = 4;
+    }
     // Short K (<= 2 chunks): an item covers several groups of weight tiles of
     // one token tile (token fragments loaded once, weight loads pipelined
     // across the groups), about 8 items per CU of expected tiles.

@@ -31,10 +31,13 @@ def test_prefill_and_large_tp_slices_take_the_tiled_kernel():
 
 
 def test_single_token_tp_slice_splits_gate_up_eight_ways():
-    # I = 256: two K chunks per down row and a short gate_up; with so few
-    # tiles the gate_up K split goes to eight waves to fill the chip.
+    # I = 256: 32 weight tiles of gate_up per expert and 8 routed rows; with
+    # so few tiles the gate_up K split goes to eight waves and each item
+    # takes one weight tile, so every CU gets a workgroup.
     p = indexed(1, 8, 384, 384, 7168, 256)
-    assert "| stream " in p and "gate_up nt=2 wk=8" in p
+    assert "| stream " in p and "gate_up nt=1 wk=8 pf=4" in p
+    # Twice the routed rows fill the CUs with 2 weight tiles and 4 waves.
+    assert "gate_up nt=2 wk=4" in indexed(2, 8, 384, 384, 7168, 256)
 
 
 def test_small_tp_slice_streams():
