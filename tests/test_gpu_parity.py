@@ -211,6 +211,18 @@ def test_indexed_full_size_sampled(spec):
     assert np.all(np.isfinite(got.view(np.int16).astype(np.float64)))
 
 
+@pytest.mark.parametrize("H,I,k", [(4224, 128, 2), (4096, 256, 1)])
+def test_single_token_deep_k_split(H, I, k):
+    """One routed token on a deep-K gate_up: the planner takes one weight
+    tile per item over 8 K-split waves (33 chunks at H = 4224: uneven wave
+    ranges of 4 and 5 chunks); the layer matches the oracle."""
+    banner(f"single token deep-K split H={H} I={I} k={k}")
+    case = small_case(31, 1, H, I, 8, 8, k)
+    got, _, _ = run_indexed(*case, E_g=8, bm=16)
+    assert "gate_up nt=1 wk=8 pf=4" in C.last_plan(), C.last_plan()
+    check_close(got, oracle.moe_layer(*case), what=f"single token H={H}")
+
+
 # ---------------------------------------------------------------------------
 # grouped layouts
 # ---------------------------------------------------------------------------
