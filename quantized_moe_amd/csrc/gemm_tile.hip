@@ -566,17 +566,9 @@ __device__ __forceinline__ void run_item_shortk(const GemmArgs& a, uint8_t* xbuf
       for (int nt = 0; nt < kNT; ++nt) {
         if (dr < 0) continue;
         const f32x4_t v = acc[nt][g];
-        const int tw = tile0 + nt;
-        if (a.gate_up) {
-          const int f0 = tw * 8 + 2 * q;
-          *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
-              pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
-        } else {
-          const int n0 = tw * 16 + 4 * q;
-          const float rw = roww[g * 16 + col];
-          *reinterpret_cast<uint2*>(a.out + dr * (int64_t)a.out_ld + n0) =
-              make_uint2(pk_bf16(v[0] * rw, v[1] * rw), pk_bf16(v[2] * rw, v[3] * rw));
-        }
+        const int f0 = (tile0 + nt) * 8 + 2 * q;
+        *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
+            pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
       }
     }
   };

@@ -321,6 +321,7 @@ __global__ void clear_status(DevStatus* s) {
 // ---------------------------------------------------------------------------
 constexpr int kCombineWaves = 4;
 constexpr int kCombinePieces = 2;
+constexpr int kRowsAux = 2;  // cache policy of the row loads: non-temporal
 
 template <int B>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
@@ -375,7 +376,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
     if (!any) continue;
     // Slots without a row load from past the buffer's end (zeros) with weight
     // 0: adding those +-0 products leaves every partial sum unchanged, and no
-    // load sits behind a branch.
+    // load sits behind a branch.  Each row is read once: non-temporal loads
+    // (TP slice T = 4096, 470 MB of rows: 115 -> 87 us).
     u32x4_t y[B][P];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
         const int v = vbase + p * 64;
         const uint32_t off = (row[u] >= 0 && v < nvec) ? (uint32_t)(row[u] * row_bytes + v * 16)
                                                         : 0xFFFFFFF0u;
-        y[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0);
+        y[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, kRowsAux);
       }
     }
 #pragma unroll
