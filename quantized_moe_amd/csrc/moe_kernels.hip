@@ -321,9 +321,15 @@ __global__ void clear_status(DevStatus* s) {
 // ---------------------------------------------------------------------------
 constexpr int kCombineWaves = 4;
 constexpr int kCombinePieces = 2;
-constexpr int kRowsAux = 2;  // cache policy of the row loads: non-temporal
+// Row buffers larger than this are loaded with the non-temporal cache policy:
+// each row is read once, and a stream bigger than the MI355X's 256 MB
+// last-level cache only evicts what later reads would hit (TP slice
+// T = 4096, 470 MB of rows: 115 -> 87 us).  Smaller buffers may still sit in
+// that cache and keep the default policy (grouped combine over 117 MB of
+// rows: 34 us with it, 40 without).
+constexpr int64_t kRowsStreamBytes = (int64_t)256 << 20;
 
-template <int B>
+template <int B, int AUX>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs a) {
   constexpr int P = kCombinePieces;
   const int nvec = a.H / 8;
@@ -376,8 +382,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
     if (!any) continue;
     // Slots without a row load from past the buffer's end (zeros) with weight
     // 0: adding those +-0 products leaves every partial sum unchanged, and no
-    // load sits behind a branch.  Each row is read once: non-temporal loads
-    // (TP slice T = 4096, 470 MB of rows: 115 -> 87 us).
+    // load sits behind a branch.
     u32x4_t y[B][P];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(CombineArgs
         const int v = vbase + p * 64;
         const uint32_t off = (row[u] >= 0 && v < nvec) ? (uint32_t)(row[u] * row_bytes + v * 16)
                                                         : 0xFFFFFFF0u;
-        y[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, kRowsAux);
+        y[u][p] = __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, AUX);
       }
     }
 #pragma unroll
@@ -438,10 +443,19 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int per_wave = 64 * kCombinePieces;
   const int64_t waves = (int64_t)a.T * ((a.H / 8 + per_wave - 1) / per_wave);
   const dim3 grid((unsigned)((waves + kCombineWaves - 1) / kCombineWaves));
-  if (waves < 1024)
-    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(64 * kCombineWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(64 * kCombineWaves), 0, stream, a);
+  const dim3 block(64 * kCombineWaves);
+  const bool stream_rows = a.n_rows * a.H * 2 > kRowsStreamBytes;
+  if (waves < 1024) {
+    if (stream_rows)
+      hipLaunchKernelGGL((combine_kernel<8, 2>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<8, 0>), grid, block, 0, stream, a);
+  } else {
+    if (stream_rows)
+      hipLaunchKernelGGL((combine_kernel<2, 2>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<2, 0>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
