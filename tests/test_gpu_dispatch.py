@@ -187,18 +187,25 @@ def test_dispatch_masked_layer_combine_matches_the_oracle_chain():
     check_close(host_bf16(out), ref, "dispatch + masked layer + combine")
 
 
-def test_combine_is_exact_on_representable_sums():
+@pytest.mark.parametrize("T,k,H,n_rows", [
+    (77, 5, 72, 50),          # fewer waves than SIMDs: all slots in one batch
+    (1100, 5, 72, 50),        # more waves: slots in batches of two
+    (40, 5, 7168, 18800),     # row buffer above 256 MB (non-temporal loads), few waves
+    (1100, 5, 7168, 18800),   # row buffer above 256 MB, more waves
+])
+def test_combine_is_exact_on_representable_sums(T, k, H, n_rows):
     """The standalone combine on small-integer rows and power-of-two weights:
     every product and partial sum is exact in fp32, so the output must be the
     exact weighted sum rounded once to bf16, bit for bit.  Slots mapped to -1
     or past n_rows are left out; a token with no slot gets 0."""
-    banner("combine: exact sums")
+    banner(f"combine: exact sums T={T} k={k} H={H} n_rows={n_rows}")
     rng = np.random.default_rng(44)
-    T, k, H, n_rows = 77, 5, 72, 50
-    vals = rng.integers(-8, 9, (n_rows, H)).astype(np.float32)
-    rows_bits = oracle.f32_to_bf16(vals)
     f2r = rng.integers(-1, n_rows + 3, T * k).astype(np.int32)
     f2r[:k] = -1                                          # token 0: no slot
+    used = np.unique(f2r[(f2r >= 0) & (f2r < n_rows)])
+    vals = rng.integers(-8, 9, (used.size, H)).astype(np.float32)   # rows in `used` order
+    rows_bits = np.zeros((n_rows, H), np.uint16)
+    rows_bits[used] = oracle.f32_to_bf16(vals)
     w = (2.0 ** rng.integers(-3, 2, (T, k))).astype(np.float32)
     out = C.chord_moe_combine(dev_bf16(rows_bits), dev(f2r), dev(w))
     torch.cuda.synchronize()
@@ -207,5 +214,5 @@ def test_combine_is_exact_on_representable_sums():
         for j in range(k):
             r = f2r[t * k + j]
             if 0 <= r < n_rows:
-                exact[t] += float(w[t, j]) * vals[r]
+                exact[t] += float(w[t, j]) * vals[np.searchsorted(used, r)]
     assert np.array_equal(host_bf16(out), oracle.f32_to_bf16(exact.astype(np.float32)))
