@@ -191,7 +191,13 @@ chord_status chord_w4a16_pack(int mode, int role, const int32_t* qweight, const 
  * Routing alignment (indexed layout)
  * ------------------------------------------------------------------------- */
 
-/* Minimum sorted_ids length: T*k + E_l*(block_m - 1). */
+/* Minimum sorted_ids length: T*k + E_l*(block_m - 1), a bound that holds for
+ * any routing (every slot local, every expert ending in a partial block).  The
+ * indexed layer consumes buffers of this oversize length as they are, without
+ * reading the routed count back to the host ([Novita] §"vLLM-Integration":
+ * the indexed fast path takes the oversize alignment buffers with trusted
+ * routing validation off and stays graph-capturable).  Returns 0 for bad
+ * arguments (T < 0, k < 1, num_local_experts < 1, block_m < 1). */
 int64_t chord_moe_align_max_padded(int T, int k, int num_local_experts, int block_m);
 
 /* Workspace bytes chord_moe_align needs for these sizes. */
@@ -318,13 +324,29 @@ chord_status chord_moe_combine(const chord_bf16* rows, int64_t n_rows, int H,
 int chord_w4a16_moe_indexed_block_m(int T, int k, int E_g, int E_l, int H, int I);
 
 /* Workspace bytes for a layer call.  rows = max_padded (indexed), M
- * (contiguous) or E*max_m (masked); T and k are used by the indexed mode. */
+ * (contiguous) or E*max_m (masked); T and k are used by the indexed mode.
+ * The pages define no workspace; it exists so that a layer call allocates
+ * nothing and reads nothing back, which keeps the default indexed path
+ * capturable in a graph ([Novita] §"vLLM-Integration").  It holds the device
+ * status words and tile list, h [rows, I] bf16 and, for the indexed mode, the
+ * per-slot down outputs; the caller owns it and may reuse it across calls on
+ * one stream.  Returns 0 for bad arguments. */
 size_t chord_w4a16_moe_workspace_bytes(int mode, int T, int k, int E_l, int H, int I,
                                        int64_t rows);
 
 /*
  * Indexed layer: out[t] = bf16( sum over local j of topk_weights[t,j] * y_tj ),
  * y_tj = W2_e( bf16( silu(W1_e x_t) * (W3_e x_t) ) ), e = topk_ids[t,j] - expert_begin.
+ *
+ * The indexed family ([Novita] §"Zwei Kernel-Familien": the path that takes
+ * vLLM's sorted_ids / expert_ids / num_tokens_padded routing; §"Kernel-
+ * Optimierungen / Indizierte Kernel": one family serving EP8 prefill, TP8
+ * single-instance and EP8 decode, its schedule tuned by tokens per expert;
+ * [aihirek] §"Ket kulon kernelcsalad").  Activations stay unpadded: padding
+ * lives in the index list as the sentinel T*k (Abb. 3 of [Novita]).  The
+ * alignment is consumed on the device, oversize buffers included, with no
+ * host readback unless CHORD_FLAG_VALIDATE asks for the trusted-routing check
+ * ([Novita] §"vLLM-Integration").
  *
  * x:        device bf16 [T, H].
  * w13, w2:  handles packed with CHORD_MODE_INDEXED, roles GATE_UP (N=2I, K=H)

@@ -161,6 +161,7 @@ struct CombineArgs {
   int T, k, H;
   int expert_begin, num_experts;
   int64_t n_rows;
+  int64_t read_bytes;  // expected row bytes read (0: the whole row buffer)
   uint16_t* out;
 };
 

@@ -321,12 +321,14 @@ __global__ void clear_status(DevStatus* s) {
 // ---------------------------------------------------------------------------
 constexpr int kCombineWaves = 4;
 constexpr int kCombinePieces = 2;
-// Row buffers larger than this are loaded with the non-temporal cache policy:
-// each row is read once, and a stream bigger than the MI355X's 256 MB
-// last-level cache only evicts what later reads would hit (TP slice
-// T = 4096, 470 MB of rows: 115 -> 87 us).  Smaller buffers may still sit in
-// that cache and keep the default policy (grouped combine over 117 MB of
-// rows: 34 us with it, 40 without).
+// Combines that read more row bytes than this load them with the
+// non-temporal cache policy: each row is read once, and a stream bigger than
+// the MI355X's 256 MB last-level cache only evicts what later reads would hit
+// (TP slice T = 4096, 470 MB of rows: 115 -> 87 us).  Smaller reads may still
+// hit rows that cache holds and keep the default policy (grouped combine over
+// 117 MB of rows: 34 us with it, 40 without).  The bytes are those the call
+// expects to read (the indexed layer's y buffer has a row per slot, of which
+// only the local ones are read), else the whole row buffer.
 constexpr int64_t kRowsStreamBytes = (int64_t)256 << 20;
 
 template <int B, int AUX>
@@ -444,7 +446,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t waves = (int64_t)a.T * ((a.H / 8 + per_wave - 1) / per_wave);
   const dim3 grid((unsigned)((waves + kCombineWaves - 1) / kCombineWaves));
   const dim3 block(64 * kCombineWaves);
-  const bool stream_rows = a.n_rows * a.H * 2 > kRowsStreamBytes;
+  const bool stream_rows = (a.read_bytes > 0 ? a.read_bytes : a.n_rows * a.H * 2) > kRowsStreamBytes;
   if (waves < 1024) {
     if (stream_rows)
       hipLaunchKernelGGL((combine_kernel<8, 2>), grid, block, 0, stream, a);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -112,13 +113,35 @@ const EnvOverrides& env() {
 }
 
 // ---- planner and plan cache ------------------------------------------------
+// Every byte of a key is a named field (the explicit `pad` keeps the int64
+// aligned without compiler padding), so hashing and comparing the raw bytes
+// is well defined; keys are only built by make_key, which zero-fills first.
 struct PlanKey {
-  int mode, T, k, E_g, E_l, H, I, hint, cus;
-  int ov[8];  // schedule override fields (kernel, tokens, gu_nt, gu_wk, dn_nt, dn_wk, prefetch,
-              // tile_split)
+  int32_t mode, T, k, E_g, E_l, H, I, hint, cus;
+  int32_t ov[8];  // schedule override fields (kernel, tokens, gu_nt, gu_wk, dn_nt, dn_wk,
+                  // prefetch, tile_split)
+  int32_t pad;
   int64_t rows;
   bool operator==(const PlanKey& o) const { return memcmp(this, &o, sizeof(*this)) == 0; }
 };
+static_assert(sizeof(PlanKey) == 18 * 4 + 8 && offsetof(PlanKey, rows) == 18 * 4,
+              "PlanKey must have no padding bytes");
+PlanKey make_key(int mode, int T, int k, int E_g, int E_l, int H, int I, int hint, int cus,
+                 int64_t rows) {
+  PlanKey key;
+  memset(&key, 0, sizeof(key));
+  key.mode = mode;
+  key.T = T;
+  key.k = k;
+  key.E_g = E_g;
+  key.E_l = E_l;
+  key.H = H;
+  key.I = I;
+  key.hint = hint;
+  key.cus = cus;
+  key.rows = rows;
+  return key;
+}
 void fill_override(PlanKey& key, const chord_schedule* s) {
   if (!s) return;
   key.ov[0] = s->kernel;
@@ -215,6 +238,7 @@ Plan make_plan(const PlanKey& key) {
   // (K > 256; the short-K kernel has no split), and no override or
   // environment switch may have turned it off.  It costs a fixup launch
   // after each tiled GEMM, so near-uniform layouts do without.
+  // (The workspace holds partial slots for masked calls only.)
   p.tile_ksplit = (kernel & 2) && key.mode == kMasked && key.H / kChunkK > 2 &&
                   key.I / kChunkK > 2 && key.ov[7] != 1 && env().tile_split != 1;
 
@@ -418,8 +442,10 @@ WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   off = align_up(off + (size_t)w.max_tiles_b * sizeof(TileDesc), 256);
   w.split_tiles = off;
   off = align_up(off + (size_t)kMaxSplitTiles * sizeof(TileDesc), 256);
+  // K-split partial slots: only masked calls split outsized tiles along K.
   w.partials = off;
-  off = align_up(off + (size_t)kSplitCapSlots * kPartialSlotFloats * sizeof(float), 256);
+  if (mode == kMasked)
+    off = align_up(off + (size_t)kSplitCapSlots * kPartialSlotFloats * sizeof(float), 256);
   w.h = off;
   off = align_up(off + (size_t)rows * I * 2, 256);
   w.y = off;
@@ -780,9 +806,9 @@ chord_status chord_w4a16_moe_plan(int mode, int T, int k, int num_global_experts
     return fail(CHORD_ERR_INVALID_ARGUMENT, "grouped calls take no schedule override");
   if (override && !override_in_range(override))
     return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
-  PlanKey key{mode, mode == kMasked ? 0 : T, mode == kMasked ? 0 : k,
-              mode == kIndexed ? num_global_experts : 0, E_l, H, I, hint,
-              num_cus > 0 ? num_cus : 256, {0}, rows};
+  PlanKey key = make_key(mode, mode == kMasked ? 0 : T, mode == kMasked ? 0 : k,
+                         mode == kIndexed ? num_global_experts : 0, E_l, H, I, hint,
+                         num_cus > 0 ? num_cus : 256, rows);
   fill_override(key, override);
   const Plan plan = get_plan(key);
   snprintf(buf, n, "%s: %s", mode == kIndexed ? "indexed" : mode == kContiguous ? "contiguous" : "masked",
@@ -1076,7 +1102,7 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
   int cus = 0;
   CHORD_CHECK(check_device(&cus));
-  PlanKey key{kIndexed, T, k, num_global_experts, E_l, H, I, block_m, cus, {0}, max_padded};
+  PlanKey key = make_key(kIndexed, T, k, num_global_experts, E_l, H, I, block_m, cus, max_padded);
   fill_override(key, override);
   const Plan plan = get_plan(key);
   set_plan_text("indexed", plan);
@@ -1106,6 +1132,12 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
   c.num_experts = E_l;
   c.n_rows = (int64_t)T * k;
   c.out = out;
+  // The rows actually read are the local slots, about T*k*E_l/E_g of the
+  // T*k the buffer is sized for.
+  {
+    const int eg = num_global_experts > E_l ? num_global_experts : E_l;
+    c.read_bytes = (int64_t)((double)T * k * E_l / eg * H * 2);
+  }
   HIP_TRY(launch_combine(c, st), "combine launch");
   timer.mark(4);
   timer.finish();
@@ -1144,8 +1176,8 @@ chord_status chord_w4a16_moe_grouped_contiguous(
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
   int cus = 0;
   CHORD_CHECK(check_device(&cus));
-  const PlanKey key{kContiguous, T, k, 0, E_l, H, I, (int)std::min<int64_t>(valid_m_hint, 1 << 30),
-                    cus, {0}, M};
+  const PlanKey key = make_key(kContiguous, T, k, 0, E_l, H, I,
+                               (int)std::min<int64_t>(valid_m_hint, 1 << 30), cus, M);
   const Plan plan = get_plan(key);
   set_plan_text("contiguous", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1205,7 +1237,7 @@ chord_status chord_w4a16_moe_grouped_masked(const chord_bf16* a, int E, int max_
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
   int cus = 0;
   CHORD_CHECK(check_device(&cus));
-  const PlanKey key{kMasked, 0, 0, 0, E, H, I, expected_m, cus, {0}, rows};
+  const PlanKey key = make_key(kMasked, 0, 0, 0, E, H, I, expected_m, cus, rows);
   const Plan plan = get_plan(key);
   set_plan_text("masked", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);

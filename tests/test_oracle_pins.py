@@ -516,6 +516,148 @@ def test_planted_mistakes_fail_pins(monkeypatch, mutation):
 
 
 # ----------------------------------------------------------------------------
+# grouped layouts: per-row weights and the row subset
+# ----------------------------------------------------------------------------
+
+def brute_row(x_row_bits, e, q13, s13, q2, s2):
+    """y of one row through expert e by scalar fp64 loops from the definition
+    (dequant with exact rational rounding, gate rows first, h rounded to bf16).
+    Returns the unrounded fp64 y [H]."""
+    H = x_row_bits.shape[0]
+    I = q13.shape[1] // 2
+    xv = [bits_to_float(int(b)) for b in x_row_bits]
+
+    def W(q, s, n, kk):
+        code = nibble(int(q[e, n, kk // 8]), kk % 8)
+        return bf16_round_exact((code - 8) * bits_to_float(int(s[e, n, kk // 32])))
+
+    gu = [sum(W(q13, s13, n, kk) * xv[kk] for kk in range(H)) for n in range(2 * I)]
+    h = [bf16_round_exact(gu[i] / (1.0 + math.exp(-gu[i])) * gu[I + i]) for i in range(I)]
+    return [sum(W(q2, s2, n, i) * h[i] for i in range(I)) for n in range(H)]
+
+
+def _row_weight_case():
+    rng = np.random.default_rng(91)
+    E, H, I = 3, 64, 32
+    x, ids, _, q13, s13, q2, s2, eb = tiny_workload(92, T=9, H=H, I=I, E_g=3, E_l=E, k=2,
+                                                    expert_begin=0)
+    a, m_idx, _, _ = G.build_contiguous(ids, x, 0, E, align=8)
+    # fp32 weights that are not powers of two, so rounding y before the
+    # weight (double rounding) differs from rounding once after it
+    rw = rng.uniform(0.1, 1.0, a.shape[0]).astype(np.float32)
+    valid = np.nonzero(m_idx >= 0)[0]
+    rows = rng.permutation(valid)[: max(4, valid.size // 2)]   # shuffled subset
+    return a, m_idx, q13, s13, q2, s2, rw, rows
+
+
+def _contiguous_row_pin_holds(fn):
+    """fn = grouped_contiguous (or a mutation of it) against brute force:
+    output i is row rows[i] of expert m_indices[rows[i]], times the weight of
+    that absolute row, rounded to bf16 once."""
+    a, m_idx, q13, s13, q2, s2, rw, rows = _row_weight_case()
+    got = om.bf16_to_f64(fn(a, m_idx, q13, s13, q2, s2, row_weights=rw, rows=rows))
+    if got.shape != (len(rows), a.shape[1]):
+        return False
+    for i, r in enumerate(rows):
+        y = brute_row(a[r], int(m_idx[r]), q13, s13, q2, s2)
+        exp = [bf16_round_exact(float(rw[r]) * v) for v in y]
+        if not np.array_equal(got[i], np.array(exp)):
+            return False
+    return True
+
+
+def test_contiguous_row_weights_and_row_subset_brute_force():
+    assert _contiguous_row_pin_holds(oracle.grouped_contiguous)
+
+
+def test_contiguous_row_subset_without_weights_brute_force():
+    """rows= alone: each listed row (shuffled order) equals the brute-force
+    y of that row, rounded once; unlisted rows are not in the output."""
+    a, m_idx, q13, s13, q2, s2, _, rows = _row_weight_case()
+    got = om.bf16_to_f64(oracle.grouped_contiguous(a, m_idx, q13, s13, q2, s2, rows=rows))
+    assert got.shape == (len(rows), a.shape[1])
+    for i, r in enumerate(rows):
+        exp = [bf16_round_exact(v) for v in brute_row(a[r], int(m_idx[r]), q13, s13, q2, s2)]
+        assert np.array_equal(got[i], np.array(exp))
+
+
+def _masked_row_pin_holds(fn):
+    rng = np.random.default_rng(93)
+    E, max_m, H, I = 3, 5, 64, 32
+    a3 = G.draw_activations(rng, E * max_m, H).reshape(E, max_m, H)
+    mm = np.array([5, 0, 3], np.int32)
+    q13, s13 = G.draw_weights(rng, E, 2 * I, H)
+    q2, s2 = G.draw_weights(rng, E, H, I)
+    rw = rng.uniform(0.1, 1.0, (E, max_m)).astype(np.float32)
+    got = om.bf16_to_f64(fn(a3, mm, q13, s13, q2, s2, row_weights=rw))
+    for e in range(E):
+        for r in range(max_m):
+            row = got[e * max_m + r]
+            if r >= mm[e]:
+                if not np.all(row == 0):           # the oracle leaves invalid rows 0
+                    return False
+                continue
+            y = brute_row(a3[e, r], e, q13, s13, q2, s2)
+            exp = [bf16_round_exact(float(rw[e, r]) * v) for v in y]
+            if not np.array_equal(row, np.array(exp)):
+                return False
+    return True
+
+
+def test_masked_row_weights_brute_force():
+    assert _masked_row_pin_holds(oracle.grouped_masked)
+
+
+def _mutated_contiguous(kind):
+    orig = om.grouped_contiguous
+
+    def by_position(a, m, q13, s13, q2, s2, row_weights=None, rows=None):
+        # weight i of the subset taken for row rows[i]
+        rw = np.array(row_weights, copy=True)
+        rw[np.asarray(rows)] = np.asarray(row_weights)[: len(rows)]
+        return orig(a, m, q13, s13, q2, s2, row_weights=rw, rows=rows)
+
+    def after_rounding(a, m, q13, s13, q2, s2, row_weights=None, rows=None):
+        y = orig(a, m, q13, s13, q2, s2, rows=rows)
+        w = np.asarray(row_weights, dtype=np.float64)[np.asarray(rows)][:, None]
+        return om.f64_to_bf16(om.bf16_to_f64(y) * w)
+
+    def subset_ignored(a, m, q13, s13, q2, s2, row_weights=None, rows=None):
+        return orig(a, m, q13, s13, q2, s2, row_weights=row_weights, rows=np.sort(rows))
+
+    return {"by_position": by_position, "after_rounding": after_rounding,
+            "subset_order": subset_ignored}[kind]
+
+
+def _mutated_masked(kind):
+    orig = om.grouped_masked
+
+    def flat_index(a3, mm, q13, s13, q2, s2, row_weights=None):
+        # weight of row r of expert e read as the (e + r)-th weight of a flat list
+        E, max_m = np.asarray(row_weights).shape
+        flat = np.asarray(row_weights).reshape(-1)
+        rw = np.array([[flat[e + r] for r in range(max_m)] for e in range(E)], np.float32)
+        return orig(a3, mm, q13, s13, q2, s2, row_weights=rw)
+
+    def after_rounding(a3, mm, q13, s13, q2, s2, row_weights=None):
+        y = om.bf16_to_f64(orig(a3, mm, q13, s13, q2, s2))
+        w = np.asarray(row_weights, dtype=np.float64).reshape(-1)[:, None]
+        return om.f64_to_bf16(y * w)
+
+    return {"flat_index": flat_index, "after_rounding": after_rounding}[kind]
+
+
+@pytest.mark.parametrize("kind", ["by_position", "after_rounding", "subset_order"])
+def test_planted_row_weight_mistakes_fail_the_contiguous_pin(kind):
+    assert not _contiguous_row_pin_holds(_mutated_contiguous(kind))
+
+
+@pytest.mark.parametrize("kind", ["flat_index", "after_rounding"])
+def test_planted_row_weight_mistakes_fail_the_masked_pin(kind):
+    assert not _masked_row_pin_holds(_mutated_masked(kind))
+
+
+# ----------------------------------------------------------------------------
 # dispatch into the grouped layouts
 # ----------------------------------------------------------------------------
 

@@ -93,3 +93,34 @@ def test_query_rejects_null_buffer():
     # A short buffer is filled and terminated, not overrun.
     assert C.lib.chord_w4a16_moe_plan(0, 64, 8, 384, 48, 7168, 2048, 16, 1024, 0, None, buf, 8) == 0
     assert buf.value == b"indexed"
+
+
+def test_plan_cache_holds_one_entry_per_descriptor():
+    """Identical descriptors hit the memoised plan whatever the caller's stack
+    held before (the key has no indeterminate bytes): in a fresh process with
+    CHORD_LOG=1, which logs each plan the cache computes, repeated queries from
+    different call depths and with stack garbage in between compute each
+    distinct descriptor once."""
+    import os
+    import subprocess
+    import sys
+    code = r'''
+import ctypes, random
+from quantized_moe_amd import chord as C
+def q(T):
+    return C.chord_w4a16_moe_plan(C.MODE_INDEXED, T, 8, 384, 48, 7168, 2048, 16,
+                                  C.chord_moe_align_max_padded(T, 8, 48, 16))
+def deep(n, T):
+    junk = ctypes.create_string_buffer(bytes(random.getrandbits(8) for _ in range(256)))
+    return q(T) if n == 0 else deep(n - 1, T)
+for i in range(60):
+    deep(i % 13, 64 if i % 2 else 8192)
+    C.chord_w4a16_moe_plan(C.MODE_MASKED, 0, 0, 0, 48, 7168, 2048, 18, 48 * 256)
+'''
+    env = dict(os.environ, CHORD_LOG="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[chord] plan")]
+    assert len(lines) == 3, lines
