@@ -2,8 +2,8 @@
 
 Alignment tensors must match bit for bit; the bf16 layer output must match
 within |gpu - ref| <= 2e-2 * rms(ref) + 1e-2 * |ref| (tests/tolerance.py).
-Full-size workloads are checked on sampled tokens / rows the oracle can
-compute one by one, in the same launch configuration the benchmark uses.
+The full-size workloads are covered by tests/test_gpu_full_size.py against
+expected values the oracle wrote beforehand.
 """
 
 import numpy as np
@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from moe_inputs import gen as G
-from moe_inputs.configs import TINY, DECODE, PREFILL, tp_slice, masked_zipf
+from moe_inputs.configs import TINY
 from tests.gpu_util import banner, dev, dev_bf16, host, host_bf16
 from tests.tolerance import check_close
 
@@ -180,37 +180,6 @@ def test_indexed_validate_flag_reports_bad_expert_ids():
     torch.cuda.synchronize()
 
 
-def _sample_tokens(ids, eb, E_l, n, seed):
-    has = np.nonzero(np.any((ids >= eb) & (ids < eb + E_l), axis=1))[0]
-    none = np.nonzero(~np.any((ids >= eb) & (ids < eb + E_l), axis=1))[0]
-    rng = np.random.default_rng(seed)
-    pick = list(rng.choice(has, size=min(n, has.size), replace=False))
-    if none.size:
-        pick.append(int(none[0]))
-    return sorted(int(t) for t in pick)
-
-
-@pytest.mark.parametrize("spec", [DECODE, tp_slice(1), tp_slice(32), tp_slice(512), tp_slice(4096),
-                                  PREFILL], ids=lambda s: s.name)
-def test_indexed_full_size_sampled(spec):
-    banner(f"indexed full size {spec.name}: drawing inputs")
-    wl = G.make_workload(spec)
-    banner(f"indexed full size {spec.name}: GPU run")
-    got, _, _ = run_indexed(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2,
-                            wl.expert_begin, wl.E_g, bm=C.chord_w4a16_moe_indexed_block_m(
-                                wl.T, wl.k, wl.E_g, wl.E_l, wl.H, wl.I))
-    toks = _sample_tokens(wl.topk_ids, wl.expert_begin, wl.E_l, 3 if wl.T > 1000 else 6, 0)
-    banner(f"indexed full size {spec.name}: oracle on tokens {toks}")
-    ref = oracle.moe_layer(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2,
-                           wl.expert_begin, tokens=toks)
-    st = check_close(got[toks], ref, spec.name)
-    banner(f"  {st}")
-    # tokens with no local slot are exactly zero
-    none = ~np.any((wl.topk_ids >= wl.expert_begin) & (wl.topk_ids < wl.expert_begin + wl.E_l), axis=1)
-    assert np.all(got[none] == 0)
-    assert np.all(np.isfinite(got.view(np.int16).astype(np.float64)))
-
-
 @pytest.mark.parametrize("H,I,k", [(4224, 128, 2), (4096, 256, 1)])
 def test_single_token_deep_k_split(H, I, k):
     """One routed token on a deep-K gate_up: the planner takes one weight
@@ -257,30 +226,6 @@ def test_contiguous_row_weights():
     ref = oracle.grouped_contiguous(a, m_idx, q13, s13, q2, s2, row_weights=rw)
     valid = m_idx >= 0
     check_close(host_bf16(rows)[valid], ref[valid])
-
-
-def test_contiguous_prefill_same_draw_sampled():
-    from quantized_moe_amd.moe import W4A16MoE
-    wl = G.make_workload(PREFILL)
-    banner("contiguous prefill: dispatch")
-    a, m_idx, f2r, nvalid = G.build_contiguous(wl.topk_ids, wl.x, 0, wl.E_l)
-    layer = W4A16MoE(dev(wl.q13), dev_bf16(wl.s13), dev(wl.q2), dev_bf16(wl.s2),
-                     mode=C.MODE_CONTIGUOUS)
-    banner(f"contiguous prefill: GPU run M={a.shape[0]}")
-    rows, _ = layer.contiguous(dev_bf16(a), dev(m_idx), nvalid)
-    torch.cuda.synchronize()
-    rows_h = host_bf16(rows)
-    rng = np.random.default_rng(1)
-    valid_rows = np.nonzero(m_idx >= 0)[0]
-    # rows of two experts, including each segment's last row (ragged tail)
-    pick = set(rng.choice(valid_rows, 6, replace=False).tolist())
-    for e in (0, wl.E_l - 1):
-        seg = np.nonzero(m_idx == e)[0]
-        pick |= {int(seg[0]), int(seg[-1])}
-    pick = sorted(pick)
-    banner(f"contiguous prefill: oracle rows {pick}")
-    ref = oracle.grouped_contiguous(a, m_idx, wl.q13, wl.s13, wl.q2, wl.s2, rows=pick)
-    check_close(rows_h[pick], ref, "contiguous prefill rows")
 
 
 def test_masked_small():
@@ -347,31 +292,6 @@ def test_masked_validate_reports_overflowing_counts():
     for e in range(E):
         sl = slice(e * max_m, e * max_m + clamped[e])
         check_close(got[sl], ref[sl])
-
-
-@pytest.mark.parametrize("E_l", [48, 96, 24])
-def test_masked_zipf_full_size_sampled(E_l):
-    spec = masked_zipf(E_l)
-    banner(f"masked full size {spec.name}: drawing")
-    wl = G.make_workload(spec)
-    from quantized_moe_amd.moe import W4A16MoE
-    layer = W4A16MoE(dev(wl.q13), dev_bf16(wl.s13), dev(wl.q2), dev_bf16(wl.s2), mode=C.MODE_MASKED)
-    banner(f"masked full size {spec.name}: GPU run")
-    out = layer.masked(dev_bf16(wl.a3), dev(wl.masked_m), wl.expected_m)
-    torch.cuda.synchronize()
-    got = host_bf16(out)
-    # hottest expert (several tiles, ragged tail) and a cold one
-    order = np.argsort(-wl.masked_m)
-    for e in (int(order[0]), int(order[len(order) // 2])):
-        m = int(wl.masked_m[e])
-        if m == 0:
-            continue
-        rows = sorted({0, m - 1, m // 2})
-        banner(f"masked full size: oracle expert {e} rows {rows} of {m}")
-        sub = wl.a3[e:e + 1, rows]
-        ref = oracle.grouped_masked(sub, np.array([len(rows)], np.int32), wl.q13[e:e + 1],
-                                    wl.s13[e:e + 1], wl.q2[e:e + 1], wl.s2[e:e + 1])
-        check_close(got[[e * wl.max_m + r for r in rows]], ref, f"masked e={e}")
 
 
 # ---------------------------------------------------------------------------
