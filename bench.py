@@ -1,6 +1,6 @@
 """Benchmark of the W4A16 MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME,...]
 
 A step is one pass of the whole hot path over one synthetic batch: routing
 alignment (chord_moe_align) and the layer (tile build, gate_up GEMM + SiLU*mul,
@@ -11,16 +11,20 @@ steps so that every step streams its weights from HBM, not from the 256 MB
 Infinity Cache.  Before the W warm-up steps, untimed steps run for at least
 --prewarm-ms (default 300 ms): the GPU raises its clocks over tens of
 milliseconds of sustained work, so without it the timed steps would measure
-the ramp (decode: about 221 instead of 193 µs per call), not the steady state
+the ramp (decode: about 221 instead of 193 us per call), not the steady state
 of a busy serving loop.
 
-Prints ONE JSON line (rank 0).  `roofline` reports the dominant kernel
-(gate_up for decode-shaped calls, the bigger of the two GEMMs otherwise)
-against HBM (8 TB/s) or dense BF16 MFMA (2.5 PFLOP/s) from its algorithmic
-bytes / FLOPs and its average duration, measured with HIP events recorded by
-the library on the launch stream over a second pass of the same K steps (event
-records between kernels would add microseconds to the timed pass itself).  `cpu_baseline` times
-the CPU oracle on a bounded sample of the same workload.
+Prints ONE JSON line (rank 0) for --workload (default: the decode EP share).
+`roofline` reports the dominant kernel (the slower of the two GEMMs) against
+HBM (8 TB/s) or dense BF16 MFMA (2.5 PFLOP/s), whichever bound the workload's
+arithmetic intensity selects, from its algorithmic bytes / FLOPs and its
+average duration, measured with HIP events recorded by the library on the
+launch stream over a second pass of the same K steps (event records between
+kernels would add microseconds to the timed pass itself); `detail` carries
+the other fraction of the same kernel too.  Each workload named by --also
+(default: the indexed prefill EP share) is measured the same way and reported
+under `detail.also`.  `cpu_baseline` times the CPU oracle on a bounded sample
+of the main workload.
 """
 
 from __future__ import annotations
@@ -43,6 +47,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 W_BYTES = 0.5625          # one packed nibble + a bf16 scale per 32 weights
 DEFAULT_WORKLOAD = "kimi_decode_T64_ep48of384_top8"
+DEFAULT_ALSO = "kimi_prefill_T8192_ep48of384_top8"
 
 
 def parse():
@@ -51,8 +56,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="comma-separated workloads measured after the main one and reported "
+                         "under detail.also ('' or 'none': no others)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work (whole experts are run until it is spent)")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed steps for at least this long before the warm-up steps: the "
                          "GPU's clocks ramp up over tens of ms of sustained work, and the timed "
@@ -144,12 +153,14 @@ def algorithmic_work(wl):
 # the same step replayed from a HIP graph (launch-latency-bound small shapes)
 # ---------------------------------------------------------------------------
 
-def graph_replay_us(step, n_rep, steps):
+def graph_replay_us(step, n_rep, steps, prewarm_ms):
     """Captures one call per weight replica (alignment + layer, the timed step)
     into a HIP graph and returns the average time per call over `steps`
     replays, bracketed by HIP events on the capturing stream.  The layer's
     default path enqueues no memset, no allocation and no host sync, so it is
-    capturable as is."""
+    capturable as is.  Capture leaves the GPU idle for tens of milliseconds,
+    long enough for its clocks to fall, so the graph is replayed untimed for
+    `prewarm_ms` first, as the eager steps are."""
     import torch
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -163,9 +174,11 @@ def graph_replay_us(step, n_rep, steps):
         for i in range(n_rep):
             step(i)
     torch.cuda.synchronize()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < prewarm_ms:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -247,76 +260,82 @@ def grouped_io(C, wl, rows, steps, dev, d, dbf):
 # CPU oracle baseline (bounded sample)
 # ---------------------------------------------------------------------------
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s):
+    """The CPU oracle on whole experts of the workload, each dequantised once
+    with all of its routed rows, until `budget_s` is spent; the time scales to
+    the call by active experts (the oracle's work per expert is dominated by
+    the dequantisation of its weights, which does not depend on its row
+    count), and the combine over the sampled slots is timed with it."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        blas = None
     if wl.layout == "masked":
-        order = [e for e in np.argsort(-wl.masked_m) if wl.masked_m[e] > 0]
-        done_rows, t0 = 0, time.perf_counter()
-        n_e = 0
-        for e in order:
-            m = int(wl.masked_m[e])
-            oracle.grouped_masked(wl.a3[e:e + 1, :m], np.array([m], np.int32), wl.q13[e:e + 1],
-                                  wl.s13[e:e + 1], wl.q2[e:e + 1], wl.s2[e:e + 1])
-            done_rows += m
-            n_e += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        el = time.perf_counter() - t0
-        total = int(wl.masked_m.sum())
-        scale = total / max(done_rows, 1)
-        sample = f"oracle on {n_e} of {int((wl.masked_m > 0).sum())} active experts " \
-                 f"({done_rows} of {total} rows), scaled by rows"
+        rows_of = {e: np.arange(int(wl.masked_m[e])) for e in range(wl.E_l) if wl.masked_m[e] > 0}
     else:
-        ids = wl.topk_ids - wl.expert_begin
-        local = (ids >= 0) & (ids < wl.E_l)
-        tokens = np.nonzero(np.any(local, axis=1))[0]
-        rng = np.random.default_rng(0)
-        order = rng.permutation(tokens)
-        done, slots, t0 = [], 0, time.perf_counter()
-        step = 1
-        while len(done) < len(order):
-            batch = order[len(done):len(done) + step]
-            oracle.moe_layer(wl.x, wl.topk_ids, wl.topk_weights, wl.q13, wl.s13, wl.q2, wl.s2,
-                             wl.expert_begin, tokens=batch)
-            done.extend(batch.tolist())
-            slots += int(local[batch].sum())
-            if time.perf_counter() - t0 > budget_s:
-                break
-            step = min(step * 2, 64)
-        el = time.perf_counter() - t0
-        total = int(local.sum())
-        scale = total / max(slots, 1)
-        sample = f"oracle on {len(done)} of {len(tokens)} tokens with a local slot " \
-                 f"({slots} of {total} routed slots), scaled by slots"
-    return {"value": el * scale * 1e6, "unit": "us/call", "cores": int(threads), "kind": "oracle",
-            "sample": sample, "measured_s": round(el, 3)}
+        flat = wl.topk_ids.reshape(-1).astype(np.int64) - wl.expert_begin
+        rows_of = {e: np.nonzero(flat == e)[0] for e in range(wl.E_l) if np.any(flat == e)}
+    order = list(np.random.default_rng(0).permutation(sorted(rows_of)))
+    x = None if wl.layout == "masked" else oracle.bf16_to_f64(wl.x)
+    ys, done, t0 = {}, 0, time.perf_counter()
+    for e in order:
+        w13 = oracle.dequant_f64(wl.q13[e], wl.s13[e])
+        w2 = oracle.dequant_f64(wl.q2[e], wl.s2[e])
+        if wl.layout == "masked":
+            xr = oracle.bf16_to_f64(wl.a3[e, :len(rows_of[e])])
+        else:
+            xr = x[rows_of[e] // wl.k]
+        y = oracle.expert_mlp(xr, w13, w2)
+        if wl.layout != "masked":
+            for r, i in enumerate(rows_of[e].tolist()):
+                ys[(i // wl.k, i % wl.k)] = y[r]
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    if wl.layout != "masked":
+        toks = sorted({t for t, _ in ys})
+        sub_ids = np.full_like(wl.topk_ids, -1)          # only the sampled slots are local
+        for t, j in ys:
+            sub_ids[t, j] = wl.topk_ids[t, j]
+        oracle.combine(ys, sub_ids, wl.topk_weights, wl.expert_begin, wl.E_l, wl.H, toks)
+    el = time.perf_counter() - t0
+    n_active = len(rows_of)
+    sample = (f"oracle (fp64 NumPy) on {done} of {n_active} active experts, each dequantised once "
+              f"with all its routed rows" + ("" if wl.layout == "masked" else ", plus the combine "
+              "of the sampled slots") + (f"; scaled by experts ({n_active}/{done})"
+                                         if done < n_active else "; the whole call"))
+    return {"value": round(el * n_active / max(done, 1) * 1e6, 1), "unit": "us/call",
+            "cores": cores, "kind": "oracle", "sample": sample, "measured_s": round(el, 3),
+            "cpu_model": cpu_model(), "blas_threads": blas}
 
 
 # ---------------------------------------------------------------------------
+# one workload: build, time, kernel-time, roofline
+# ---------------------------------------------------------------------------
 
-def main():
-    args = parse()
-    if args.copy_probe > 0:
-        copy_probe(args.copy_probe, args.steps)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N>1 is not supported "
-                                   "(the layer takes one GPU's expert share, no collectives)"}))
-        sys.exit(2)
+def measure(spec, args, C, dev, with_graph=False, grouped=False):
+    """Times `args.steps` steps of `spec` (after the clock pre-warm and
+    `args.warmup` untimed steps) and the per-stage kernel durations of a
+    second pass; returns (config, result dict, workload)."""
     import torch
     from moe_inputs import gen as G
-    from moe_inputs.configs import workload_by_name
-    from quantized_moe_amd import chord as C
     from quantized_moe_amd.moe import W4A16MoE
 
-    spec = workload_by_name(args.workload)
     wl = G.make_workload(spec)
-    dev = torch.device("cuda:0")
 
     def d(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -333,7 +352,7 @@ def main():
     del q13, s13, q2, s2
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
+    out_rows = None
     if wl.layout == "indexed":
         x, ids, w = dbf(wl.x), d(wl.topk_ids), d(wl.topk_weights)
         bm = C.chord_w4a16_moe_indexed_block_m(wl.T, wl.k, wl.E_g, wl.E_l, wl.H, wl.I)
@@ -410,49 +429,82 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     work = algorithmic_work(wl)
     avg = [m / max(calls, 1) for m in stage_ms]           # ms per call per stage
-    gu_ms, dn_ms = avg[1], avg[2]
-    decode_shaped = work["layer_flops"] / max(work["layer_bytes"], 1) < 2.5e15 / 8e12
-    if decode_shaped:
-        name, dur, alg, = "gate_up", gu_ms, work["gate_up_bytes"]
-        if dn_ms > gu_ms:
-            name, dur, alg = "down", dn_ms, work["down_bytes"]
-        achieved = alg / (dur * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(spec.name, name), "algorithmic_bytes": int(alg),
-                "avg_ms": round(dur, 5)}
-    else:
-        name, dur, alg = "gate_up", gu_ms, work["gate_up_flops"]
-        if dn_ms > gu_ms:
-            name, dur, alg = "down", dn_ms, work["down_flops"]
-        achieved = alg / (dur * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(spec.name, name),
-                "algorithmic_flops": alg, "avg_ms": round(dur, 5)}
-    layer_ms = sum(avg)
-    extra = {"stage_ms": [round(m, 5) for m in avg], "layer_kernels_ms": round(layer_ms, 5),
-             "layer_hbm_GBs": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
-             "layer_TFLOPs": round(work["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
-             "routed_rows": work["R"], "active_experts": work["active"], "plan": plan,
-             "weight_replicas": n_rep,
-             "prewarm": {"ms": round(prewarm_ms, 1), "steps": prewarm_steps}}
+    name = "down" if avg[2] > avg[1] else "gate_up"
+    dur = avg[2] if name == "down" else avg[1]
+    alg_b, alg_f = work[f"{name}_bytes"], work[f"{name}_flops"]
+    gbs = alg_b / (dur * 1e-3) / 1e9
+    tfs = alg_f / (dur * 1e-3) / 1e12
+    hbm = {"bound": "hbm", "kernel": name, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "traffic": measured_traffic(spec.name, name), "algorithmic_bytes": int(alg_b),
+           "avg_ms": round(dur, 5)}
+    mfma = {"bound": "mfma", "kernel": name, "achieved": round(tfs, 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+            "traffic": hbm["traffic"], "algorithmic_flops": alg_f, "avg_ms": round(dur, 5)}
+    # The bound the layer's arithmetic intensity selects (HBM below the
+    # 312 FLOP/B balance point of 2.5 PFLOP/s over 8 TB/s).
+    hbm_bound = work["layer_flops"] / max(work["layer_bytes"], 1) < 2.5e15 / 8e12
+    roof, other = (hbm, mfma) if hbm_bound else (mfma, hbm)
+    layer_gbs = work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9
+    layer_tfs = work["layer_flops"] / (ms_per_step * 1e-3) / 1e12
+    res = {"us_per_call": round(ms_per_step * 1e3, 2), "ms_per_step": round(ms_per_step, 5),
+           "roofline": roof, "roofline_other": {k: other[k] for k in
+                                                ("bound", "kernel", "achieved", "unit", "frac")},
+           "stage_ms": [round(m, 5) for m in avg], "layer_kernels_ms": round(sum(avg), 5),
+           "layer_algorithmic_bytes": int(work["layer_bytes"]),
+           "layer_algorithmic_flops": work["layer_flops"],
+           "layer_hbm_GBs": round(layer_gbs, 1), "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+           "layer_TFLOPs": round(layer_tfs, 2),
+           "layer_mfma_frac": round(layer_tfs / BF16_PEAK_TFLOPS, 4),
+           "routed_rows": work["R"], "active_experts": work["active"], "plan": plan,
+           "weight_replicas": n_rep,
+           "prewarm": {"ms": round(prewarm_ms, 1), "steps": prewarm_steps}}
+    if grouped and wl.layout == "contiguous":
+        res["grouped_io"] = grouped_io(C, wl, out_rows, args.steps, dev, d, dbf)
+    if with_graph and wl.layout == "indexed" and wl.T <= 64:
+        res["graph_us_per_call"] = graph_replay_us(step, n_rep, args.steps, args.prewarm_ms)
+    del layers, step
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return config, res, wl
 
-    if wl.layout == "contiguous":
-        extra["grouped_io"] = grouped_io(C, wl, out_rows, args.steps, dev, d, dbf)
-    if wl.layout == "indexed" and wl.T <= 64:
-        extra["graph_us_per_call"] = graph_replay_us(step, n_rep, args.steps)
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, args.steps)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N>1 is not supported "
+                                   "(the layer takes one GPU's expert share, no collectives)"}))
+        sys.exit(2)
+    import torch
+    from moe_inputs.configs import workload_by_name
+    from quantized_moe_amd import chord as C
+
+    dev = torch.device("cuda:0")
+    spec = workload_by_name(args.workload)
+    config, res, wl = measure(spec, args, C, dev, with_graph=True, grouped=True)
+
+    also = {}
+    for name in [n for n in args.also.split(",") if n and n != "none" and n != args.workload]:
+        _, r, _ = measure(workload_by_name(name), args, C, dev)
+        also[name] = r
 
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, args.cpu_budget)
 
-    line = {"metric": METRIC, "value": round(ms_per_step * 1e3, 2), "unit": "us/call",
+    detail = {k: v for k, v in res.items() if k not in ("us_per_call", "ms_per_step", "roofline")}
+    if also:
+        detail["also"] = also
+    line = {"metric": METRIC, "value": res["us_per_call"], "unit": "us/call",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(ms_per_step, 5), "higher_is_better": False, "scaling": "weak",
+            "ms_per_step": res["ms_per_step"], "higher_is_better": False, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": config, "roofline": roof, "cpu_baseline": cpu, "detail": extra}
+            "config": config, "roofline": res["roofline"], "cpu_baseline": cpu, "detail": detail}
     print(json.dumps(line), flush=True)
 
 
