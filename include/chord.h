@@ -376,6 +376,42 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
                                      size_t ws_bytes, const chord_schedule* override,
                                      uint32_t flags, void* stream);
 
+/* Scratch bytes the allocation-free indexed entry point holds per GPU. */
+#define CHORD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * Allocation-free variant of chord_w4a16_moe_indexed, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and error behaviour as chord_w4a16_moe_indexed, minus the
+ * workspace: the call's scratch (status words, tile list, h and the per-slot
+ * down outputs) lives in a static device array of CHORD_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library holds on each GPU it runs on, from the first such
+ * call on that GPU until the process ends.  It calls no hipMalloc / hipFree
+ * and creates no stream or event (the stage profiler is not recorded; a
+ * kernel-3 schedule, which needs a side stream, is rejected).
+ *
+ * Limit: calls whose workspace (chord_w4a16_moe_workspace_bytes) exceeds
+ * CHORD_NOALLOC_SCRATCH_BYTES return CHORD_ERR_WORKSPACE before anything is
+ * enqueued; the decode EP share (T = 64, 48 of 384 experts, H = 7168,
+ * I = 2048) and the TP slices up to T = 512 fit.
+ *
+ * Every allocation-free call on a GPU shares that GPU's array, and each call
+ * rewrites what it reads (nothing has to start at zero): calls that overlap
+ * on one GPU, from other streams or threads, race on it and must be
+ * serialised by the caller.
+ */
+chord_status chord_w4a16_moe_indexed_noalloc(const chord_bf16* x, int T, int H, int I,
+                                             const chord_w4a16_weight* w13,
+                                             const chord_w4a16_weight* w2,
+                                             const int32_t* topk_ids, const float* topk_weights,
+                                             int k, int expert_begin, int num_global_experts,
+                                             const int32_t* sorted_ids, const int32_t* expert_ids,
+                                             const int32_t* num_tokens_post_padded,
+                                             int64_t max_padded, int block_m, chord_bf16* out,
+                                             const chord_schedule* override, uint32_t flags,
+                                             void* stream);
+
 /*
  * Grouped contiguous layer ([Novita] §"Gruppierte SM90-Kernel", Abb. 3): rows
  * concatenated per expert in segments padded to 128-row boundaries.

@@ -28,7 +28,7 @@ EXPORTED = [
     "chord_profile_enable", "chord_profile_reset", "chord_profile_read",
     "chord_w4a16_packed_bytes", "chord_w4a16_pack", "chord_moe_align_max_padded",
     "chord_moe_align_workspace_bytes", "chord_moe_align", "chord_w4a16_moe_indexed_block_m",
-    "chord_w4a16_moe_workspace_bytes", "chord_w4a16_moe_indexed",
+    "chord_w4a16_moe_workspace_bytes", "chord_w4a16_moe_indexed", "chord_w4a16_moe_indexed_noalloc",
     "chord_w4a16_moe_grouped_contiguous", "chord_w4a16_moe_grouped_masked",
     "chord_moe_dispatch_contiguous_rows", "chord_moe_dispatch_workspace_bytes",
     "chord_moe_dispatch_contiguous", "chord_moe_dispatch_masked", "chord_moe_combine",
@@ -80,6 +80,8 @@ def _load():
         "chord_w4a16_moe_workspace_bytes": (SZ, [I, I, I, I, I, I, I64]),
         "chord_w4a16_moe_indexed": (I, [P, I, I, I, WP, WP, P, P, I, I, I, P, P, P, I64, I, P, P, SZ,
                                         ctypes.POINTER(Schedule), U32, P]),
+        "chord_w4a16_moe_indexed_noalloc": (I, [P, I, I, I, WP, WP, P, P, I, I, I, P, P, P, I64, I, P,
+                                                ctypes.POINTER(Schedule), U32, P]),
         "chord_w4a16_moe_grouped_contiguous": (I, [P, I64, P, I64, WP, WP, I, I, P, P, I, I, P, P, P,
                                                    P, SZ, ctypes.POINTER(Schedule), U32, P]),
         "chord_w4a16_moe_grouped_masked": (I, [P, I, I, P, I, WP, WP, I, I, P, P, P, SZ,
@@ -247,6 +249,23 @@ def chord_w4a16_moe_indexed(x, w13: PackedWeight, w2: PackedWeight, topk_ids, to
         _ptr(topk_weights), k, expert_begin, num_global_experts, _ptr(sorted_ids), _ptr(expert_ids),
         _ptr(ntpp), max_padded, block_m, _ptr(out), _ptr(workspace), workspace.numel(),
         _sched(override), flags, _stream(stream)))
+    return out
+
+
+def chord_w4a16_moe_indexed_noalloc(x, w13: PackedWeight, w2: PackedWeight, topk_ids,
+                                    topk_weights, expert_begin, num_global_experts, sorted_ids,
+                                    expert_ids, ntpp, block_m, out, override=None, flags=0,
+                                    stream=None):
+    """The allocation-free indexed layer: no workspace, and `out` must be
+    given (this wrapper allocates nothing either)."""
+    T, H = x.shape
+    I = w2.handle.k
+    k = topk_ids.shape[1]
+    _check(lib.chord_w4a16_moe_indexed_noalloc(
+        _ptr(x), T, H, I, ctypes.byref(w13.handle), ctypes.byref(w2.handle), _ptr(topk_ids),
+        _ptr(topk_weights), k, expert_begin, num_global_experts, _ptr(sorted_ids), _ptr(expert_ids),
+        _ptr(ntpp), sorted_ids.numel(), block_m, _ptr(out), _sched(override), flags,
+        _stream(stream)))
     return out
 
 

@@ -394,9 +394,9 @@ struct StageTimer {
   bool on = false;
   ProfRecord rec{};
   hipStream_t stream = nullptr;
-  explicit StageTimer(hipStream_t s) : stream(s) {
+  explicit StageTimer(hipStream_t s, bool allowed = true) : stream(s) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    on = g_prof_on;
+    on = g_prof_on && allowed;
     if (!on) return;
     for (int i = 0; i < 5; ++i) {
       if (!g_ev_pool.empty()) {
@@ -671,6 +671,35 @@ chord_status finish_validate(uint32_t flags, const WsLayout& ws, uint8_t* wsp, h
           "status readback");
   HIP_TRY(hipStreamSynchronize(stream), "stream sync");
   if (err != 0) return fail(CHORD_ERR_ROUTING, "routing validation failed (flags 0x%x)", err);
+  return CHORD_OK;
+}
+
+// ---- scratch of the allocation-free indexed entry point --------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// from the first allocation-free call until the process ends.  In host code
+// the array's name is a host-side stand-in, not a device address, so it is
+// never passed to a kernel or a copy: the device address is looked up once
+// per device (with that device current) and kept in g_scratch.  Every
+// allocation-free call on a GPU shares that GPU's array; calls that overlap
+// on one GPU (other streams, other threads) race on it.
+constexpr size_t kNoAllocScratchBytes = CHORD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch[64];
+
+chord_status noalloc_scratch(void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(CHORD_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CHORD_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
   return CHORD_OK;
 }
 
@@ -1069,16 +1098,20 @@ size_t chord_w4a16_moe_workspace_bytes(int mode, int T, int k, int E_l, int H, i
   return layer_ws(mode, T, k, E_l, H, I, rows).total;
 }
 
-chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
-                                     const chord_w4a16_weight* w13, const chord_w4a16_weight* w2,
-                                     const int32_t* topk_ids, const float* topk_weights, int k,
-                                     int expert_begin, int num_global_experts,
-                                     const int32_t* sorted_ids, const int32_t* expert_ids,
-                                     const int32_t* num_tokens_post_padded, int64_t max_padded,
-                                     int block_m, chord_bf16* out, void* workspace,
-                                     size_t ws_bytes, const chord_schedule* override,
-                                     uint32_t flags, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// The indexed layer on a given workspace.  no_alloc: the call may not create
+// HIP objects (no profiling events, no side stream for kernel 3).
+chord_status indexed_impl(const chord_bf16* x, int T, int H, int I, const chord_w4a16_weight* w13,
+                          const chord_w4a16_weight* w2, const int32_t* topk_ids,
+                          const float* topk_weights, int k, int expert_begin,
+                          int num_global_experts, const int32_t* sorted_ids,
+                          const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                          int64_t max_padded, int block_m, chord_bf16* out, void* workspace,
+                          size_t ws_bytes, const chord_schedule* override, uint32_t flags,
+                          void* stream, bool no_alloc) {
   if (T < 0 || k < 1) return fail(CHORD_ERR_INVALID_ARGUMENT, "T=%d k=%d", T, k);
   CHORD_CHECK(check_pair(w13, w2, CHORD_MODE_INDEXED, H, I));
   const int E_l = w13->num_experts;
@@ -1097,7 +1130,19 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
     return fail(CHORD_ERR_UNSUPPORTED, "T*k*H*2 exceeds 2 GiB");
   if (override && !override_in_range(override))
     return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
+  if (no_alloc && override && override->kernel == 3)
+    return fail(CHORD_ERR_INVALID_ARGUMENT,
+                "kernel 3 needs a side stream, which the allocation-free call does not create");
   const WsLayout ws = layer_ws(kIndexed, T, k, E_l, H, I, max_padded);
+  if (no_alloc && ws.total > kNoAllocScratchBytes)
+    return fail(CHORD_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                ws.total, kNoAllocScratchBytes);
+  if (no_alloc) {
+    CHORD_CHECK(check_device(nullptr));
+    CHORD_CHECK(noalloc_scratch(&workspace));
+    ws_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || ws_bytes < ws.total)
     return fail(CHORD_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, ws.total);
   int cus = 0;
@@ -1105,6 +1150,9 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
   PlanKey key = make_key(kIndexed, T, k, num_global_experts, E_l, H, I, block_m, cus, max_padded);
   fill_override(key, override);
   const Plan plan = get_plan(key);
+  if (no_alloc && plan.kernel == 3)
+    return fail(CHORD_ERR_INVALID_ARGUMENT,
+                "kernel 3 needs a side stream, which the allocation-free call does not create");
   set_plan_text("indexed", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* wsp = static_cast<uint8_t*>(workspace);
@@ -1116,7 +1164,7 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
   tb.block_m = block_m;
   tb.max_padded = max_padded;
   uint16_t* y = reinterpret_cast<uint16_t*>(wsp + ws.y);
-  StageTimer timer(st);
+  StageTimer timer(st, !no_alloc);
   CHORD_CHECK(run_expert_gemms(kIndexed, plan, ws, wsp, w13, w2, H, I, x, T, max_padded,
                                sorted_ids, k, (int64_t)T * k, nullptr, y, (int64_t)T * k, nullptr,
                                tb, st, timer));
@@ -1142,6 +1190,42 @@ chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
   timer.mark(4);
   timer.finish();
   return finish_validate(flags, ws, wsp, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+chord_status chord_w4a16_moe_indexed(const chord_bf16* x, int T, int H, int I,
+                                     const chord_w4a16_weight* w13, const chord_w4a16_weight* w2,
+                                     const int32_t* topk_ids, const float* topk_weights, int k,
+                                     int expert_begin, int num_global_experts,
+                                     const int32_t* sorted_ids, const int32_t* expert_ids,
+                                     const int32_t* num_tokens_post_padded, int64_t max_padded,
+                                     int block_m, chord_bf16* out, void* workspace,
+                                     size_t ws_bytes, const chord_schedule* override,
+                                     uint32_t flags, void* stream) {
+  g_last_error.clear();
+  return indexed_impl(x, T, H, I, w13, w2, topk_ids, topk_weights, k, expert_begin,
+                      num_global_experts, sorted_ids, expert_ids, num_tokens_post_padded,
+                      max_padded, block_m, out, workspace, ws_bytes, override, flags, stream,
+                      false);
+}
+
+chord_status chord_w4a16_moe_indexed_noalloc(const chord_bf16* x, int T, int H, int I,
+                                             const chord_w4a16_weight* w13,
+                                             const chord_w4a16_weight* w2,
+                                             const int32_t* topk_ids, const float* topk_weights,
+                                             int k, int expert_begin, int num_global_experts,
+                                             const int32_t* sorted_ids, const int32_t* expert_ids,
+                                             const int32_t* num_tokens_post_padded,
+                                             int64_t max_padded, int block_m, chord_bf16* out,
+                                             const chord_schedule* override, uint32_t flags,
+                                             void* stream) {
+  g_last_error.clear();
+  return indexed_impl(x, T, H, I, w13, w2, topk_ids, topk_weights, k, expert_begin,
+                      num_global_experts, sorted_ids, expert_ids, num_tokens_post_padded,
+                      max_padded, block_m, out, nullptr, 0, override, flags, stream, true);
 }
 
 chord_status chord_w4a16_moe_grouped_contiguous(

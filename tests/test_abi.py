@@ -170,3 +170,33 @@ def test_dispatch_and_combine_host_validation():
     assert L.chord_moe_combine(FAKE, 16, 256, None, FAKE, 4, 2, FAKE, None) == 1
     assert L.chord_moe_combine(FAKE, 1 << 22, 1024, FAKE, FAKE, 4, 2, FAKE, None) == 2
     assert L.chord_moe_combine(FAKE, 16, 256, FAKE, FAKE, 0, 2, FAKE, None) == 0   # no tokens: no-op
+
+
+def _indexed_noalloc(h13, h2, T=4, H=256, I=128, k=2, bm=16, max_padded=None, ov=None):
+    mp = max_padded if max_padded is not None else T * k + h13.num_experts * (bm - 1)
+    return C.lib.chord_w4a16_moe_indexed_noalloc(
+        FAKE, T, H, I, ctypes.byref(h13), ctypes.byref(h2), FAKE, FAKE, k, 0, 8,
+        FAKE, FAKE, FAKE, mp, bm, FAKE, ov, 0, None)
+
+
+def test_noalloc_entry_point_rejects_misuse_and_oversize_calls_on_the_host():
+    """The allocation-free call validates like the workspace one, and a call
+    whose scratch would exceed CHORD_NOALLOC_SCRATCH_BYTES (64 MiB) is
+    refused before anything touches the device."""
+    h13, h2 = _handle(0, 0), _handle(0, 1, N=256, K=128)
+    assert _indexed_noalloc(h13, h2, bm=24) == 1
+    assert _indexed_noalloc(h13, h2, max_padded=3) == 1
+    assert _indexed_noalloc(_handle(1, 0), h2) == 3
+    three = C.Schedule()
+    three.kernel = 3
+    assert _indexed_noalloc(h13, h2, ov=ctypes.byref(three)) == 1
+    assert b"side stream" in C.lib.chord_last_error()
+    assert _indexed_noalloc(h13, h2, T=0) == 0
+    # the prefill EP share: h and the per-slot rows need far more than 64 MiB
+    g13 = _handle(0, 0, E=48, N=4096, K=7168)
+    g2 = _handle(0, 1, E=48, N=7168, K=2048)
+    need = C.chord_w4a16_moe_workspace_bytes(0, 8192, 8, 48, 7168, 2048,
+                                             C.chord_moe_align_max_padded(8192, 8, 48, 16))
+    assert need > 64 << 20
+    assert _indexed_noalloc(g13, g2, T=8192, H=7168, I=2048, k=8) == 4
+    assert b"scratch" in C.lib.chord_last_error()
