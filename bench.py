@@ -2,10 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME,...]
 
-A step is one pass of the whole hot path over one synthetic batch: routing
-alignment (chord_moe_align) and the layer (tile build, gate_up GEMM + SiLU*mul,
-down GEMM, weighted combine) for the indexed layout; the layer alone for the
-grouped layouts (their row maps are the dispatcher's output).  Inputs are
+A step is one pass of the whole hot path over one synthetic batch: for the
+indexed layout routing alignment (chord_moe_align) and the layer (tile build,
+gate_up GEMM + SiLU*mul, down GEMM, weighted combine), or, where the planner
+routes the call inside the gate_up launch (block_m 0: a few thousand slots on
+the weight-streaming kernels), the layer alone, whose gate_up derives the
+per-expert rows from topk_ids itself; the layer alone for the grouped layouts
+(their row maps are the dispatcher's output).  Inputs are
 resident in HBM before the timed region.  Weight replicas are rotated across
 steps so that every step streams its weights from HBM, not from the 256 MB
 Infinity Cache.  Before the W warm-up steps, untimed steps run for at least
@@ -355,23 +358,30 @@ def measure(spec, args, C, dev, with_graph=False, grouped=False):
     out_rows = None
     if wl.layout == "indexed":
         x, ids, w = dbf(wl.x), d(wl.topk_ids), d(wl.topk_weights)
+        # block_m 0: the planner routes the call inside the gate_up launch
+        # (rows from topk_ids), so the step has no alignment launch.
         bm = C.chord_w4a16_moe_indexed_block_m(wl.T, wl.k, wl.E_g, wl.E_l, wl.H, wl.I)
-        mp = C.chord_moe_align_max_padded(wl.T, wl.k, wl.E_l, bm)
-        al_out = (torch.empty(mp, dtype=torch.int32, device=dev),
-                  torch.empty((mp + bm - 1) // bm, dtype=torch.int32, device=dev),
-                  torch.empty(1, dtype=torch.int32, device=dev))
-        al_ws = torch.empty(max(1, C.lib.chord_moe_align_workspace_bytes(wl.T, wl.k, wl.E_l, bm)),
-                            dtype=torch.uint8, device=dev)
+        mp = C.chord_moe_align_max_padded(wl.T, wl.k, wl.E_l, bm) if bm else 0
         out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
         for L in layers:
             L.workspace(C.chord_w4a16_moe_workspace_bytes(C.MODE_INDEXED, wl.T, wl.k, wl.E_l, wl.H,
                                                           wl.I, mp), dev)
+        if bm:
+            al_out = (torch.empty(mp, dtype=torch.int32, device=dev),
+                      torch.empty((mp + bm - 1) // bm, dtype=torch.int32, device=dev),
+                      torch.empty(1, dtype=torch.int32, device=dev))
+            al_ws = torch.empty(max(1, C.lib.chord_moe_align_workspace_bytes(wl.T, wl.k, wl.E_l,
+                                                                             bm)),
+                                dtype=torch.uint8, device=dev)
 
-        def step(i):
-            L = layers[i % n_rep]
-            C.chord_moe_align(ids, wl.expert_begin, wl.E_l, bm, max_padded=mp, out=al_out,
-                              workspace=al_ws)
-            L.indexed(x, ids, w, wl.expert_begin, wl.E_g, align=(*al_out, bm), out=out)
+            def step(i):
+                L = layers[i % n_rep]
+                C.chord_moe_align(ids, wl.expert_begin, wl.E_l, bm, max_padded=mp, out=al_out,
+                                  workspace=al_ws)
+                L.indexed(x, ids, w, wl.expert_begin, wl.E_g, align=(*al_out, bm), out=out)
+        else:
+            def step(i):
+                layers[i % n_rep].indexed(x, ids, w, wl.expert_begin, wl.E_g, block_m=0, out=out)
         config = {"workload": spec.name, "layout": "indexed", "T": wl.T, "H": wl.H, "I": wl.I,
                   "E_global": wl.E_g, "E_local": wl.E_l, "top_k": wl.k, "block_m": bm}
     elif wl.layout == "contiguous":

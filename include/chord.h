@@ -320,11 +320,22 @@ chord_status chord_moe_combine(const chord_bf16* rows, int64_t n_rows, int H,
 
 /* block_m the planner wants for an indexed call with these shapes (the caller
  * aligns with it before the layer call).  Token counts per expert, not total
- * tokens, decide the schedule ([Novita] TL;DR and §"H200 Prefill und TP8"). */
+ * tokens, decide the schedule ([Novita] TL;DR and §"H200 Prefill und TP8").
+ *
+ * Returns 0 when the call needs no alignment: the planner routes it inside
+ * the GEMM (the weight-streaming kernels at T*k <= 2048 slots, e.g. decode
+ * and the small TP slices): every workgroup of the gate_up launch derives
+ * the rows of its expert from topk_ids itself, so the caller may skip
+ * chord_moe_align and pass NULL alignment pointers (max_padded 0, block_m 0)
+ * to chord_w4a16_moe_indexed.  This keeps the pages' contract of an indexed
+ * path that needs no host readback ([Novita] §"vLLM-Integration") and drops
+ * the alignment launch and its dependent index loads from the critical path
+ * of the small calls. */
 int chord_w4a16_moe_indexed_block_m(int T, int k, int E_g, int E_l, int H, int I);
 
-/* Workspace bytes for a layer call.  rows = max_padded (indexed), M
- * (contiguous) or E*max_m (masked); T and k are used by the indexed mode.
+/* Workspace bytes for a layer call.  rows = max_padded (indexed; 0 for a
+ * call without alignment), M (contiguous) or E*max_m (masked); T and k are
+ * used by the indexed mode.
  * The pages define no workspace; it exists so that a layer call allocates
  * nothing and reads nothing back, which keeps the default indexed path
  * capturable in a graph ([Novita] §"vLLM-Integration").  It holds the device
@@ -357,7 +368,13 @@ size_t chord_w4a16_moe_workspace_bytes(int mode, int T, int k, int E_l, int H, i
  *           rows per expert that picks the schedule.
  * sorted_ids, expert_ids, num_tokens_post_padded, max_padded, block_m: the
  *           alignment (chord_moe_align's output contract); oversize buffers
- *           are consumed on the device without host readback.
+ *           are consumed on the device without host readback.  Not read, and
+ *           may be NULL / 0, when chord_w4a16_moe_indexed_block_m returns 0
+ *           for these shapes and no schedule override is given (a routed
+ *           call: the gate_up launch builds each expert's row list from
+ *           topk_ids in LDS; with T <= 16 and T*k <= 64 the down GEMM and
+ *           the combine also run as one launch, summing w * y in fp32 without
+ *           rounding y to bf16 first).
  * out:      device bf16 [T, H]; every row is written (rows of tokens with no
  *           local expert are 0).
  * override: NULL or a schedule override.

@@ -237,7 +237,7 @@ def chord_w4a16_moe_indexed(x, w13: PackedWeight, w2: PackedWeight, topk_ids, to
     T, H = x.shape
     I = w2.handle.k
     k = topk_ids.shape[1]
-    max_padded = sorted_ids.numel()
+    max_padded = 0 if sorted_ids is None else sorted_ids.numel()
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     ws_bytes = lib.chord_w4a16_moe_workspace_bytes(MODE_INDEXED, T, k, w13.num_experts, H, I,
@@ -264,8 +264,8 @@ def chord_w4a16_moe_indexed_noalloc(x, w13: PackedWeight, w2: PackedWeight, topk
     _check(lib.chord_w4a16_moe_indexed_noalloc(
         _ptr(x), T, H, I, ctypes.byref(w13.handle), ctypes.byref(w2.handle), _ptr(topk_ids),
         _ptr(topk_weights), k, expert_begin, num_global_experts, _ptr(sorted_ids), _ptr(expert_ids),
-        _ptr(ntpp), sorted_ids.numel(), block_m, _ptr(out), _sched(override), flags,
-        _stream(stream)))
+        _ptr(ntpp), 0 if sorted_ids is None else sorted_ids.numel(), block_m, _ptr(out),
+        _sched(override), flags, _stream(stream)))
     return out
 
 

@@ -92,7 +92,7 @@ __device__ __forceinline__ RowMap map_row(const GemmArgs& a, int expert, int64_t
       m.src = f / a.topk;
       m.dst = R;
     } else {
-      m.src = R;
+      m.src = a.h_by_slot ? f : R;
       m.dst = f;
     }
   } else if (a.layout == kContiguous) {
@@ -123,6 +123,150 @@ __device__ __forceinline__ TileDesc get_tile(const GemmArgs& a, int ti) {
   return t;
 }
 
+// Routing tables of a routed call, built in LDS by every workgroup of the
+// gate_up launch from topk_ids (T * k <= kRoutedMaxSlots): the local slots
+// grouped by expert (`list`), each expert's first and past-the-end row and
+// first tile in that list, and the expert of every tile of `tok` rows.  The
+// order of the slots inside an expert's group is not fixed: each output row
+// depends only on its own slot (h and y are stored per flat slot), so which
+// rows share a tile changes no value.  Workgroup 0 also stores the list and
+// the tiles for the down launch.
+struct Routes {
+  const int* rowoff;   // [E]: first row of each active expert in `list`
+  const int* rowend;   // [E]: past its last row
+  const int* tileoff;  // [E]: its first tile
+  const int* list;     // [n]
+  const int* tile_e;   // [tiles]
+  int ntiles;
+  int nrows;
+  int tok;
+  __device__ TileDesc tile(int ti) const {
+    const int e = tile_e[ti];
+    const int r0 = rowoff[e] + (ti - tileoff[e]) * tok;
+    const int nr = min(tok, rowend[e] - r0);
+    return TileDesc{e, r0, nr, 0, 1, 0, 0, 0};
+  }
+};
+
+__device__ Routes build_routes(const GemmArgs& a, int* lds, int tok) {
+  __shared__ int scan_tmp[17 * 2];
+  __shared__ int totals[2];
+  const int E = a.num_experts, n = a.route_n;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  int* rowoff = lds;
+  int* rowend = rowoff + E;
+  int* tileoff = rowend + E;
+  int* list = tileoff + E;
+  int* tile_e = list + n;
+  int* cnt = tile_e + n;  // [E + 2], general path only
+  int nrows, ntiles;
+  if (n <= 64) {
+    // One wave, one ballot per distinct local expert (experts in the order of
+    // their first slot): no LDS atomics, no scan.
+    if (tid < 64) {
+      const int idv = tid < n ? a.route_ids[tid] - a.route_eb : -1;
+      const bool loc = tid < n && (unsigned)idv < (unsigned)E;
+      uint64_t rem = __builtin_amdgcn_ballot_w64(loc);
+      int rows = 0, tiles = 0;
+      while (rem != 0) {
+        const int leader = __builtin_ctzll(rem);
+        const int e = __builtin_amdgcn_readlane(idv, leader);
+        const uint64_t same = __builtin_amdgcn_ballot_w64(loc && idv == e);
+        rem &= ~same;
+        const int c = __builtin_popcountll(same);
+        const int nt = (c + tok - 1) / tok;
+        if (tid == 0) {
+          rowoff[e] = rows;
+          rowend[e] = rows + c;
+          tileoff[e] = tiles;
+        }
+        if ((same >> tid) & 1ull)
+          list[rows + __builtin_popcountll(same & ((1ull << tid) - 1ull))] = tid;
+        if (tid < nt) tile_e[tiles + tid] = e;
+        rows += c;
+        tiles += nt;
+      }
+      if (tid == 0) {
+        totals[0] = rows;
+        totals[1] = tiles;
+      }
+    }
+    __syncthreads();
+    nrows = totals[0];
+    ntiles = totals[1];
+  } else {
+    for (int e = tid; e < E; e += nth) cnt[e] = 0;
+    // Local expert of this thread's slots tid + nth * u, read in batches of
+    // kIdBatch independent loads (one memory round trip per batch) and kept
+    // for the scatter pass.
+    constexpr int kIdBatch = 8;
+    const int nb = (n + nth * kIdBatch - 1) / (nth * kIdBatch);  // batches (uniform)
+    int ev[kIdBatch];
+    auto load_ids = [&](int b) {
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u) {
+        const int i = (b * kIdBatch + u) * nth + tid;
+        ev[u] = i < n ? a.route_ids[i] - a.route_eb : -1;
+      }
+    };
+    load_ids(0);
+    __syncthreads();
+    for (int b = 0; b < nb; ++b) {
+      if (b > 0) load_ids(b);
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u)
+        if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&cnt[ev[u]], 1);
+    }
+    __syncthreads();
+    // Exclusive scans of the row and tile counts: each thread owns a
+    // contiguous range of experts, one block scan over the thread sums.
+    const int per = (E + nth - 1) / nth;
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int v[2] = {0, 0}, tot[2];
+    for (int e = lo; e < hi; ++e) {
+      v[0] += cnt[e];
+      v[1] += (cnt[e] + tok - 1) / tok;
+    }
+    block_scan_excl_n<2>(v, scan_tmp, tot);
+    {
+      int r = v[0], t = v[1];
+      for (int e = lo; e < hi; ++e) {
+        rowoff[e] = r;
+        tileoff[e] = t;
+        r += cnt[e];
+        rowend[e] = r;
+        t += (cnt[e] + tok - 1) / tok;
+      }
+    }
+    __syncthreads();
+    for (int b = nb - 1; b >= 0; --b) {  // the last batch is still in registers
+      if (b < nb - 1) load_ids(b);
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u)
+        if ((unsigned)ev[u] < (unsigned)E)
+          list[rowoff[ev[u]] + atomicSub(&cnt[ev[u]], 1) - 1] = (b * kIdBatch + u) * nth + tid;
+    }
+    for (int e = tid; e < E; e += nth) {
+      const int t1 = tileoff[e] + (rowend[e] - rowoff[e] + tok - 1) / tok;
+      for (int t = tileoff[e]; t < t1; ++t) tile_e[t] = e;
+    }
+    __syncthreads();
+    nrows = tot[0];
+    ntiles = tot[1];
+  }
+  Routes r{rowoff, rowend, tileoff, list, tile_e, ntiles, nrows, tok};
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < nrows; i += nth) a.route_list[i] = list[i];
+    for (int t = tid; t < ntiles; t += nth) a.route_tiles[t] = r.tile(t);
+    if (tid == 0) {
+      DevStatus* st = const_cast<DevStatus*>(a.status);
+      st->ntiles = ntiles;
+      st->error = 0;
+    }
+  }
+  return r;
+}
+
 // A workgroup of WK waves owns NT 16-row weight tiles of one expert and up to
 // MT*16 rows of one token tile; the waves split K and reduce through LDS.
 // Per 128-wide K chunk each lane streams 16 bytes of packed codes and one
@@ -136,7 +280,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
   const int q = lane >> 4;
   const int col = lane & 15;
-  const int n_items = num_tiles(a) * a.items_per_tile;
+  // Routed gate_up: tiles and rows from the LDS tables (after the K
+  // reduction area in dynamic LDS).
+  const bool routed = a.route_ids != nullptr;
+  Routes rt{};
+  if (routed)
+    rt = build_routes(a, reinterpret_cast<int*>(red + (WK > 1 ? WK * NT * MT * 64 * 4 : 0)),
+                      MT * 16);
+  const int n_items = (routed ? rt.ntiles : num_tiles(a)) * a.items_per_tile;
   const int c_lo = (a.n_chunks * wave) / WK;
   const int c_hi = (a.n_chunks * (wave + 1)) / WK;
   const uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
@@ -147,7 +298,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int ti = item / a.items_per_tile;
     const int ng = item % a.items_per_tile;
-    const TileDesc td = get_tile(a, ti);
+    const TileDesc td = routed ? rt.tile(ti) : get_tile(a, ti);
     const int e = td.expert;
     if (e < 0) continue;  // uniform over the workgroup
 
@@ -162,7 +313,13 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
       xoff[mt] = kNoRow;
       dst[mt] = -1;
       if (m < td.nrows) {
-        const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
+        RowMap rm;
+        if (routed) {  // gate_up of a routed call: h row per flat slot
+          const int f = rt.list[td.row_begin + m];
+          rm = RowMap{f / a.topk, f};
+        } else {
+          rm = map_row(a, e, (int64_t)td.row_begin + m);
+        }
         if (rm.src >= 0) {
           xoff[mt] = (uint32_t)((rm.src * (int64_t)a.K + q * kGroup) * 2);
           dst[mt] = rm.dst;
@@ -449,10 +606,131 @@ __global__ __launch_bounds__(64) void gemm_stream_shortk(GemmArgs a) {
   }
 }
 
+// Fused down GEMM + weighted top-k combine of a routed call with at most
+// kFusedMaxTokens tokens and kFusedMaxSlots slots (the single-token TP
+// slice): one workgroup of W waves per 16-row weight tile of the output.
+// Wave w computes, for the local slots j = w, w + W, ... (in ascending flat
+// order), the tile's 16 outputs of y = W2_e h[slot] in fp32 (h is stored per
+// flat slot by the routed gate_up; the slot's row is MFMA column 0) through a
+// PF-deep ring of (slot, K chunk) steps, and leaves them in LDS.  Wave 0 then
+// adds w[t,j] * y over the local slots in ascending flat order, which is
+// ascending j for every token, and stores the tile's bf16 outputs of every
+// token; tokens without a local slot get zero.  y is not rounded to bf16
+// before the sum.  Each W2 tile of a slot's expert is read once per slot.
+// The slot lists live in registers (lane u holds the u-th entry) and are
+// read with readlane at uniform indices, so no load waits on LDS.
+template <int W, int PF>
+__global__ __launch_bounds__(64 * W) void down_combine_small(GemmArgs a) {
+  __shared__ float ys[kFusedMaxSlots][16];
+  __shared__ int slot_of[kFusedMaxSlots];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4, col = lane & 15;
+  const int n = a.route_n, NC = a.n_chunks, T = a.T;
+  const uint32_t kMaskLo = 0x000F000Fu, kMaskHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  // Lane i of every wave holds slot i's local expert and weight.
+  const int idv = lane < n ? a.route_ids[lane] - a.route_eb : -1;
+  const float wv = lane < n ? a.topk_weights[lane] : 0.f;
+  const bool loc = lane < n && (unsigned)idv < (unsigned)a.num_experts;
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(loc);
+  const int n_local = __builtin_popcountll(mask);
+  if (wave == 0 && loc) slot_of[__builtin_popcountll(mask & ((1ull << lane) - 1ull))] = lane;
+  __syncthreads();
+  // all_v: lane j holds the j-th local slot; mine_v: lane u the slot of this
+  // wave's u-th local slot (rank wave + W u).
+  const int all_v = lane < n_local ? slot_of[lane] : 0;
+  const int mine_v = wave + W * lane < n_local ? slot_of[wave + W * lane] : 0;
+  const int my_slots = wave < n_local ? (n_local - wave + W - 1) / W : 0;
+  const int nsteps = my_slots * NC;
+  const int64_t expert_bytes = (int64_t)a.n_tiles * NC * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t hres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
+
+  for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    uint4 wq[PF];
+    uint32_t sc[PF];
+    uint4 hb[PF][4];
+    // Step i of this wave: its slot i / NC, chunk i % NC; steps past the
+    // last are clamped to it (a redundant load, in bounds).
+    auto load_step = [&](int u, int i) {
+      const int ic = i < nsteps ? i : nsteps - 1;
+      const int js = ic / NC, c = ic - js * NC;
+      const int slot = __builtin_amdgcn_readlane(mine_v, js);
+      const int e = __builtin_amdgcn_readlane(idv, slot);
+      const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+      const uint32_t blk = (uint32_t)((tile * NC + c) * kBlockBytes);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+      wq[u] = make_uint4(v[0], v[1], v[2], v[3]);
+      sc[u] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+      const uint32_t hoff =
+          col == 0 ? (uint32_t)(((int64_t)slot * a.K + q * kGroup) * 2) : kNoRow;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4_t h = __builtin_amdgcn_raw_buffer_load_b128(hres, hoff, c * kChunkK * 2 + st * 16, 0);
+        hb[u][st] = make_uint4(h[0], h[1], h[2], h[3]);
+      }
+    };
+    if (nsteps > 0) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) load_step(u, u);
+    }
+    f32x4_t y = zero4;
+    for (int i0 = 0; i0 < nsteps; i0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int i = i0 + u;
+        if (i < nsteps) {
+          bf16x8_t av[4];
+          dequant_words(wq[u], dq_scale(sc[u]), kMaskLo, kMaskHi, kMagic, av);
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st], as_bf16x8(hb[u][st]), y, 0, 0, 0);
+          if (i + PF < nsteps) load_step(u, i + PF);  // refill the ring slot just consumed
+          if (i % NC == NC - 1) {  // slot done: its 16 outputs to LDS
+            const int j = wave + W * (i / NC);
+            if (col == 0) *reinterpret_cast<f32x4_t*>(&ys[j][4 * q]) = y;
+            y = zero4;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // Lane (r, tq) owns rows r of tokens tq, tq + 4, tq + 8, tq + 12.
+      const int r = lane & 15, tq = lane >> 4;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < n_local; j0 += 8) {
+        float yv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) yv[u] = j0 + u < n_local ? ys[j0 + u][r] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j0 + u >= n_local) break;
+          const int slot = __builtin_amdgcn_readlane(all_v, j0 + u);
+          const int t = slot / a.topk;
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), slot));
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            if (t == tq + 4 * m) acc[m] = __builtin_fmaf(w, yv[u], acc[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int t = tq + 4 * m;
+        if (t < T) a.out[(int64_t)t * a.out_ld + tile * 16 + r] = to_bf16(acc[m]);
+      }
+    }
+    __syncthreads();  // ys is reused by the next tile
+  }
+}
+
 template <int NT, int MT, int WK, int PF>
 hipError_t launch_stream_t(const GemmArgs& a, int grid, hipStream_t stream) {
-  const size_t lds = WK > 1 ? (size_t)WK * NT * MT * 64 * 4 * sizeof(float) : 0;
-  static const int per_cu = blocks_per_cu(gemm_stream<NT, MT, WK, PF>, 64 * WK, lds);
+  const size_t red = WK > 1 ? (size_t)WK * NT * MT * 64 * 4 * sizeof(float) : 0;
+  const size_t lds = red + (a.route_ids != nullptr ? route_lds_bytes(a.num_experts, a.route_n) : 0);
+  static const int per_cu = blocks_per_cu(gemm_stream<NT, MT, WK, PF>, 64 * WK, red);
   const int cap = per_cu * (a.num_cus > 0 ? a.num_cus : 256);
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL((gemm_stream<NT, MT, WK, PF>), dim3(grid), dim3(64 * WK), lds, stream, a);
@@ -470,10 +748,20 @@ hipError_t launch_stream_shortk_t(const GemmArgs& a, int grid, hipStream_t strea
   return hipGetLastError();
 }
 
+hipError_t launch_down_combine_small(const GemmArgs& a, hipStream_t stream) {
+  if (a.route_n > kFusedMaxSlots || a.T > kFusedMaxTokens) return hipErrorInvalidValue;
+  if (a.n_chunks <= 2)  // one ring step per chunk of a slot
+    hipLaunchKernelGGL((down_combine_small<8, 2>), dim3(a.n_tiles), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((down_combine_small<8, 4>), dim3(a.n_tiles), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArgs& a, int grid,
                        hipStream_t stream) {
   (void)kernel;
   if (a.slices_per_item > 0 && a.n_chunks <= 2) {  // short K: several weight-tile groups per item
+    if (a.route_ids != nullptr) return hipErrorInvalidValue;  // no routed short-K variant
     const int key = nt * 100 + mt * 10 + a.n_chunks;
     switch (key) {
       case 211: return launch_stream_shortk_t<2, 1, 1>(a, grid, stream);
@@ -496,6 +784,7 @@ hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArg
   CHORD_STREAM_WK(NT, MT, 1) CHORD_STREAM_WK(NT, MT, 2) CHORD_STREAM_WK(NT, MT, 4)
     CHORD_STREAM_MT(2, 1)
     CHORD_STREAM_CASE(1, 1, 8, 4)
+    CHORD_STREAM_CASE(1, 1, 8, 8)
     CHORD_STREAM_WK(2, 1, 8)
     CHORD_STREAM_MT(2, 2)
     CHORD_STREAM_MT(4, 1)

@@ -151,7 +151,29 @@ struct GemmArgs {
   int64_t out_rows;      // rows of `out` (bound)
   const float* row_weights;  // grouped down only, may be null
   int64_t n_rows_internal;   // internal row bound (h rows)
+  // Routed indexed calls: the rows of each expert come from topk_ids, not
+  // from an alignment.  The gate_up launch (route_ids set) builds the tables
+  // in LDS in every workgroup; its workgroup 0 also writes them to route_list
+  // / route_tiles (+ status->ntiles) for the down launch.  h rows are per
+  // flat slot then (h_by_slot: the down GEMM reads h[f], not h[R]).
+  const int32_t* route_ids;  // topk_ids [route_n], or null
+  int route_eb;              // expert_begin
+  int route_n;               // T * k
+  int32_t* route_list;       // [route_n]: flat slots grouped by local expert
+  TileDesc* route_tiles;     // [route_n]: tiles over route_list
+  int h_by_slot;
+  // Fused down + combine (routed calls with T <= 16, T * k <= 64): routing
+  // weights and the token count of the output [T, H].
+  const float* topk_weights;
+  int T;
 };
+constexpr int kRoutedMaxSlots = 2048;  // routed calls: T * k at most
+constexpr int kFusedMaxSlots = 64;     // fused down + combine: T * k at most
+constexpr int kFusedMaxTokens = 16;    // ... and T at most
+// LDS bytes of the routing tables of a routed gate_up launch: per expert a
+// first row, an end row, a first tile and a count; per slot a list entry and
+// at most one tile.
+inline size_t route_lds_bytes(int E, int n) { return (size_t)(4 * E + 2 + 2 * n) * sizeof(int); }
 
 struct CombineArgs {
   const uint16_t* rows;     // y [*, H] bf16
@@ -217,6 +239,10 @@ hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArg
 // 4 weight tiles per wave, 256 output rows per workgroup; N a multiple of 64).
 hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_tile_split_fixup(const GemmArgs& a, hipStream_t stream);
+// Fused down GEMM + weighted combine of a routed call with T <= 16 and
+// T * k <= 64: out[t] = bf16(sum over local j, ascending, of w[t,j] * y_tj),
+// every row of out written.
+hipError_t launch_down_combine_small(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_gather_contiguous(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_gather_masked(const DispatchArgs& a, hipStream_t stream);

@@ -92,6 +92,7 @@ struct EnvOverrides {
   int tile_split = 0;  // tiled kernel: 1 turns the K split of outsized tiles off
   int stream_wgs = 0;  // streaming kernel: workgroups per CU (0: balanced default)
   int prefetch = 0;
+  int routed = 1;  // 0: routed indexed calls off (every indexed call reads the alignment)
   bool log = false;
 };
 const EnvOverrides& env() {
@@ -106,6 +107,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_TILE_SPLIT")) o.tile_split = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_STREAM_WGS")) o.stream_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_ROUTED")) o.routed = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
     return o;
   }();
@@ -180,6 +182,8 @@ struct Plan {
   int max_tiles_b;   // big-tile list capacity
   int split_rows;    // kernel 3: experts with >= split_rows rows take the tiled kernel
   bool tile_ksplit;  // tiled kernel: outsized tiles may be split along K
+  bool routed;       // indexed: rows from topk_ids inside the gate_up launch (no alignment read)
+  bool fused;        // routed: down GEMM and combine in one launch
   int cus;
   GemmPlan gu, dn;    // streaming GEMMs
   GemmPlan gut, dnt;  // tiled GEMMs
@@ -270,6 +274,20 @@ Plan make_plan(const PlanKey& key) {
     p.dnt = tgemm(key.H, key.I);
   }
 
+  // Routed indexed calls (weight-streaming family chosen by the planner, a
+  // few thousand slots at most): every gate_up workgroup builds the
+  // per-expert row lists from topk_ids in LDS, so no alignment launch and no
+  // dependent chain of index loads precede the weight stream; h and y are
+  // stored per flat slot.  With at most 16 tokens and 64 slots the down GEMM
+  // and the combine run as one launch.
+  const int64_t slots = (int64_t)key.T * key.k;
+  // The gate_up K must span more than 2 chunks: with K <= 256 the streaming
+  // GEMM runs its short-K variant, which takes its tiles from the alignment.
+  p.routed = kernel == 1 && key.mode == kIndexed && key.ov[0] == 0 && env().kernel == 0 &&
+             env().routed != 0 && slots >= 1 && slots <= kRoutedMaxSlots &&
+             key.H / kChunkK > 2;
+  p.fused = p.routed && slots <= kFusedMaxSlots && key.T <= kFusedMaxTokens;
+
   // Streaming GEMMs.
   const double tok_small = kernel == 3 ? std::min(tok_e, kSplitRows - 1) : tok_e;
   int mt = (int)((tok_small + 15.0) / 16.0);
@@ -279,8 +297,9 @@ Plan make_plan(const PlanKey& key) {
   p.mt = mt;
   p.tile_tokens = mt * 16;
   // key.hint carries block_m for indexed calls.
-  p.block_tiles = kernel == 1 && key.mode == kIndexed && key.hint == p.tile_tokens;
+  p.block_tiles = !p.routed && kernel == 1 && key.mode == kIndexed && key.hint == p.tile_tokens;
   p.max_tiles = kernel == 2 ? 0
+                : p.routed ? (int)std::min<int64_t>(slots, slots / p.tile_tokens + key.E_l)
                 : p.block_tiles ? (int)((key.rows + key.hint - 1) / key.hint)
                                 : max_tiles_for(key.rows, key.E_l, p.tile_tokens);
   const int ov_pf = key.ov[6] ? key.ov[6] : env().prefetch;
@@ -328,7 +347,7 @@ Plan make_plan(const PlanKey& key) {
     // gate_up: 11.9 -> 10.3 us).
     if (g.wk == 8 && tiles_guess * (N / 16) <= key.cus) {
       g.nt = 1;
-      g.pf = 4;
+      g.pf = env().prefetch == 8 ? 8 : 4;
     }
     // Short K (<= 2 chunks): an item covers several groups of weight tiles of
     // one token tile (token fragments loaded once, weight loads pipelined
@@ -355,10 +374,11 @@ Plan make_plan(const PlanKey& key) {
   int n = std::min(cap, snprintf(p.text, sizeof(p.text), "tok_e=%.1f", tok_e));
   if (kernel & 1)
     n += snprintf(p.text + n, sizeof(p.text) - n,
-                  " | stream tiles=%s of %d rows: gate_up nt=%d wk=%d pf=%d, down nt=%d wk=%d pf=%d"
+                  " | stream tiles=%s of %d rows: gate_up nt=%d wk=%d pf=%d, %s nt=%d wk=%d pf=%d"
                   " groups/item %d",
-                  p.block_tiles ? "blocks" : "list", p.tile_tokens, p.gu.nt, p.gu.wk, p.gu.pf,
-                  p.dn.nt, p.dn.wk, p.dn.pf, p.dn.slices);
+                  p.routed ? "routed" : p.block_tiles ? "blocks" : "list", p.tile_tokens, p.gu.nt,
+                  p.gu.wk, p.gu.pf, p.fused ? "down+combine" : "down", p.dn.nt, p.dn.wk, p.dn.pf,
+                  p.dn.slices);
   n = std::min(cap, n);
   if (kernel & 2)
     snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d, %d waves (slices/item %d, %d)%s",
@@ -376,6 +396,16 @@ Plan get_plan(const PlanKey& key) {
   if (env().log) fprintf(stderr, "[chord] plan mode=%d T=%d E_l=%d: %s\n", key.mode, key.T, key.E_l,
                          p.text);
   return p;
+}
+
+// Whether an indexed call with these shapes (and override) is routed: the
+// planner's choice of the weight-streaming family at <= kRoutedMaxSlots
+// slots, which depends on neither block_m, the buffer sizes nor the CU count.
+bool routed_call(int T, int k, int E_g, int E_l, int H, int I, const chord_schedule* ov) {
+  if (T < 1 || k < 1 || E_l < 1 || E_l > kMaxExperts || H <= 0 || I <= 0) return false;
+  PlanKey key = make_key(kIndexed, T, k, E_g, E_l, H, I, 0, 256, 0);
+  fill_override(key, ov);
+  return get_plan(key).routed;
 }
 
 // ---- kernel-stage profiling (HIP events on the caller's stream) -----------
@@ -423,12 +453,18 @@ struct StageTimer {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t status, tiles, tiles_b, split_tiles, partials, h, y, total;
+  size_t status, tiles, tiles_b, split_tiles, partials, route_list, h, y, total;
   int max_tiles, max_tiles_b, max_slices;
 };
 
+// rows: the alignment's max_padded (indexed; 0 when the call is routed and
+// passes no alignment), M (contiguous) or E*max_m (masked).  Indexed layouts
+// also fit a routed call: h and the tile list hold at least T*k rows, and the
+// routed slot list takes T*k ints.
 WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   WsLayout w{};
+  const int64_t slots = mode == kIndexed ? (int64_t)T * k : 0;
+  rows = std::max(rows, slots);
   w.max_tiles = max_tiles_for(rows, E_l, 16);
   // Big tiles, plus up to 3 extra entries per K-split tile.
   w.max_tiles_b = max_tiles_for(rows, E_l, kTileTokens) + 3 * kMaxSplitTiles;
@@ -446,6 +482,8 @@ WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   w.partials = off;
   if (mode == kMasked)
     off = align_up(off + (size_t)kSplitCapSlots * kPartialSlotFloats * sizeof(float), 256);
+  w.route_list = off;
+  off = align_up(off + (size_t)slots * sizeof(int32_t), 256);
   w.h = off;
   off = align_up(off + (size_t)rows * I * 2, 256);
   w.y = off;
@@ -568,6 +606,16 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   return hipStreamWaitEvent(stream, ss->join, 0);
 }
 
+// The routing of a routed indexed call (plan.routed): what the gate_up launch
+// derives its rows from, and for the fused down + combine its output.
+struct RouteCall {
+  const int32_t* topk_ids = nullptr;
+  const float* topk_weights = nullptr;
+  int expert_begin = 0;
+  int T = 0;
+  uint16_t* out = nullptr;  // [T, H] (fused only)
+};
+
 // Shared GEMM sequence: tiles -> gate_up -> down.
 chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, uint8_t* wsp,
                               const chord_w4a16_weight* w13, const chord_w4a16_weight* w2, int H,
@@ -575,7 +623,8 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
                               int64_t rows_internal, const int32_t* sorted_ids, int topk,
                               int64_t n_flat, const int32_t* m_indices, uint16_t* down_out,
                               int64_t down_rows, const float* row_weights, TileBuildArgs tb,
-                              hipStream_t stream, StageTimer& timer) {
+                              hipStream_t stream, StageTimer& timer,
+                              const RouteCall* route = nullptr) {
   // Buffer resources address their source with 32-bit offsets.
   const int64_t kMaxBuf = ((int64_t)1 << 31) - 1;
   if (bsrc_rows * H * 2 > kMaxBuf || rows_internal * I * 2 > kMaxBuf ||
@@ -605,7 +654,9 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   tb.tiles_b = tiles_b;
   tb.status = status;
   timer.mark(0);
-  if (plan.block_tiles) {
+  if (plan.routed) {
+    // no tile builder: the gate_up launch routes itself
+  } else if (plan.block_tiles) {
     HIP_TRY(launch_check_blocks(tb, stream), "block check launch");
   } else {
     HIP_TRY(launch_build_tiles(tb, stream), "tile builder launch");
@@ -644,6 +695,16 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.out_ld = I;
   g.out_rows = rows_internal;
   g.row_weights = nullptr;
+  if (plan.routed) {
+    // Rows from topk_ids; h per flat slot.  Workgroup 0 leaves the slot
+    // list and the tiles in the workspace for the down launch.
+    g.tiles = nullptr;
+    g.route_ids = route->topk_ids;
+    g.route_eb = route->expert_begin;
+    g.route_n = (int)n_flat;
+    g.route_list = reinterpret_cast<int32_t*>(wsp + ws.route_list);
+    g.route_tiles = tiles;
+  }
   HIP_TRY(launch_planned(plan, true, g, tiles_b, stream), "gate_up launch");
   timer.mark(2);
 
@@ -659,6 +720,21 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   g.out_ld = H;
   g.out_rows = down_rows;
   g.row_weights = row_weights;
+  if (plan.routed) {
+    g.route_ids = nullptr;
+    g.tiles = tiles;                       // written by the gate_up launch
+    g.sorted_ids = g.route_list;
+    g.h_by_slot = 1;
+    if (plan.fused) {
+      g.route_ids = route->topk_ids;
+      g.topk_weights = route->topk_weights;
+      g.T = route->T;
+      g.out = route->out;
+      HIP_TRY(launch_down_combine_small(g, stream), "down+combine launch");
+      timer.mark(3);
+      return CHORD_OK;
+    }
+  }
   HIP_TRY(launch_planned(plan, false, g, tiles_b, stream), "down launch");
   timer.mark(3);
   return CHORD_OK;
@@ -829,8 +905,9 @@ chord_status chord_w4a16_moe_plan(int mode, int T, int k, int num_global_experts
   if (E_l < 1 || E_l > kMaxExperts || H <= 0 || I <= 0 || H % kChunkK != 0 || I % kChunkK != 0 ||
       rows < 0 || num_cus < 0 || hint < 0 || T < 0 || k < 0 || num_global_experts < 0)
     return fail(CHORD_ERR_INVALID_ARGUMENT, "bad call descriptor");
-  if (mode == kIndexed && (T < 1 || k < 1 || !valid_bm(hint)))
-    return fail(CHORD_ERR_INVALID_ARGUMENT, "indexed plans need T, k and a block_m of 16..128");
+  if (mode == kIndexed && (T < 1 || k < 1 || (hint != 0 && !valid_bm(hint))))
+    return fail(CHORD_ERR_INVALID_ARGUMENT,
+                "indexed plans need T, k and a block_m of 16..128 (0: no alignment)");
   if (mode != kIndexed && override)
     return fail(CHORD_ERR_INVALID_ARGUMENT, "grouped calls take no schedule override");
   if (override && !override_in_range(override))
@@ -1084,7 +1161,7 @@ chord_status chord_moe_combine(const chord_bf16* rows, int64_t n_rows, int H,
 }
 
 int chord_w4a16_moe_indexed_block_m(int T, int k, int E_g, int E_l, int H, int I) {
-  (void)H; (void)I;
+  if (routed_call(T, k, E_g, E_l, H, I, nullptr)) return 0;  // no alignment needed
   // Expected rows per expert under uniform routing; a block of 16 or 32 rows
   // is then one tile of the weight-streaming GEMM.
   const int eg = E_g > 0 ? E_g : (E_l > 0 ? E_l : 1);
@@ -1116,20 +1193,30 @@ chord_status indexed_impl(const chord_bf16* x, int T, int H, int I, const chord_
   CHORD_CHECK(check_pair(w13, w2, CHORD_MODE_INDEXED, H, I));
   const int E_l = w13->num_experts;
   if (T == 0) return CHORD_OK;
-  if (!x || !topk_ids || !topk_weights || !sorted_ids || !expert_ids || !num_tokens_post_padded ||
-      !out)
+  if (!x || !topk_ids || !topk_weights || !out)
     return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (!valid_bm(block_m))
-    return fail(CHORD_ERR_INVALID_ARGUMENT, "block_m=%d (16, 32, 64 or 128)", block_m);
-  if (max_padded < chord_moe_align_max_padded(T, k, E_l, block_m))
-    return fail(CHORD_ERR_INVALID_ARGUMENT, "max_padded=%lld below T*k + E_l*(block_m-1)",
-                (long long)max_padded);
-  if ((int64_t)T * k >= ((int64_t)1 << 30) || max_padded >= ((int64_t)1 << 31))
+  if ((int64_t)T * k >= ((int64_t)1 << 30))
     return fail(CHORD_ERR_UNSUPPORTED, "routing tensors too large");
-  if ((int64_t)T * k * H * 2 > INT32_MAX)  // y rows are read through a 32-bit buffer offset
-    return fail(CHORD_ERR_UNSUPPORTED, "T*k*H*2 exceeds 2 GiB");
   if (override && !override_in_range(override))
     return fail(CHORD_ERR_INVALID_ARGUMENT, "schedule override out of range");
+  // A routed call derives its rows from topk_ids and reads no alignment.
+  const bool routed = routed_call(T, k, num_global_experts, E_l, H, I, override);
+  if (routed) {
+    max_padded = 0;
+    block_m = 0;
+  } else {
+    if (!sorted_ids || !expert_ids || !num_tokens_post_padded)
+      return fail(CHORD_ERR_INVALID_ARGUMENT, "null pointer argument (this call reads the alignment)");
+    if (!valid_bm(block_m))
+      return fail(CHORD_ERR_INVALID_ARGUMENT, "block_m=%d (16, 32, 64 or 128)", block_m);
+    if (max_padded < chord_moe_align_max_padded(T, k, E_l, block_m))
+      return fail(CHORD_ERR_INVALID_ARGUMENT, "max_padded=%lld below T*k + E_l*(block_m-1)",
+                  (long long)max_padded);
+    if (max_padded >= ((int64_t)1 << 31))
+      return fail(CHORD_ERR_UNSUPPORTED, "routing tensors too large");
+  }
+  if ((int64_t)T * k * H * 2 > INT32_MAX)  // y rows are read through a 32-bit buffer offset
+    return fail(CHORD_ERR_UNSUPPORTED, "T*k*H*2 exceeds 2 GiB");
   if (no_alloc && override && override->kernel == 3)
     return fail(CHORD_ERR_INVALID_ARGUMENT,
                 "kernel 3 needs a side stream, which the allocation-free call does not create");
@@ -1156,6 +1243,8 @@ chord_status indexed_impl(const chord_bf16* x, int T, int H, int I, const chord_
   set_plan_text("indexed", plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* wsp = static_cast<uint8_t*>(workspace);
+  if (plan.routed != routed)
+    return fail(CHORD_ERR_HIP, "internal: routed plan mismatch");
   TileBuildArgs tb{};
   tb.num_experts = E_l;
   tb.validate = (flags & CHORD_FLAG_VALIDATE) ? 1 : 0;
@@ -1165,9 +1254,21 @@ chord_status indexed_impl(const chord_bf16* x, int T, int H, int I, const chord_
   tb.max_padded = max_padded;
   uint16_t* y = reinterpret_cast<uint16_t*>(wsp + ws.y);
   StageTimer timer(st, !no_alloc);
-  CHORD_CHECK(run_expert_gemms(kIndexed, plan, ws, wsp, w13, w2, H, I, x, T, max_padded,
-                               sorted_ids, k, (int64_t)T * k, nullptr, y, (int64_t)T * k, nullptr,
-                               tb, st, timer));
+  RouteCall rc;
+  rc.topk_ids = topk_ids;
+  rc.topk_weights = topk_weights;
+  rc.expert_begin = expert_begin;
+  rc.T = T;
+  rc.out = reinterpret_cast<uint16_t*>(out);
+  CHORD_CHECK(run_expert_gemms(kIndexed, plan, ws, wsp, w13, w2, H, I, x, T,
+                               std::max<int64_t>(max_padded, (int64_t)T * k), sorted_ids, k,
+                               (int64_t)T * k, nullptr, y, (int64_t)T * k, nullptr, tb, st, timer,
+                               &rc));
+  if (plan.fused) {  // the down launch already combined into out
+    timer.mark(4);
+    timer.finish();
+    return finish_validate(flags, ws, wsp, st);
+  }
   CombineArgs c{};
   c.rows = y;
   c.topk_ids = topk_ids;

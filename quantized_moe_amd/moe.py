@@ -40,19 +40,24 @@ class W4A16MoE:
                 block_m: Optional[int] = None, align=None, out=None, override=None, flags=0,
                 stream=None):
         """Aligns the routing (unless ``align`` = (sorted_ids, expert_ids,
-        ntpp, block_m) is given) and runs the indexed layer."""
+        ntpp, block_m) is given, or the planner routes the call inside the
+        GEMM: block_m 0) and runs the indexed layer."""
         assert self.mode == C.MODE_INDEXED
         T, k = topk_ids.shape
         if align is None:
-            bm = block_m or C.chord_w4a16_moe_indexed_block_m(T, k, num_global_experts or self.E_l,
-                                                             self.E_l, self.H, self.I)
-            sorted_ids, expert_ids, ntpp = C.chord_moe_align(topk_ids, expert_begin, self.E_l, bm,
-                                                             stream=stream)
+            bm = block_m if block_m is not None else C.chord_w4a16_moe_indexed_block_m(
+                T, k, num_global_experts or self.E_l, self.E_l, self.H, self.I)
+            if bm == 0 and override is None:
+                sorted_ids = expert_ids = ntpp = None
+            else:
+                bm = bm or 16
+                sorted_ids, expert_ids, ntpp = C.chord_moe_align(topk_ids, expert_begin, self.E_l,
+                                                                 bm, stream=stream)
         else:
             sorted_ids, expert_ids, ntpp, bm = align
-        ws = self.workspace(C.chord_w4a16_moe_workspace_bytes(C.MODE_INDEXED, T, k, self.E_l,
-                                                             self.H, self.I, sorted_ids.numel()),
-                            x.device)
+        ws = self.workspace(C.chord_w4a16_moe_workspace_bytes(
+            C.MODE_INDEXED, T, k, self.E_l, self.H, self.I,
+            0 if sorted_ids is None else sorted_ids.numel()), x.device)
         return C.chord_w4a16_moe_indexed(x, self.w13, self.w2, topk_ids, topk_weights, expert_begin,
                                          num_global_experts, sorted_ids, expert_ids, ntpp, bm,
                                          out=out, workspace=ws, override=override, flags=flags,

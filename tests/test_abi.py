@@ -39,7 +39,9 @@ def test_packed_bytes_and_bounds():
     assert C.chord_w4a16_packed_bytes(0, 1, 1, 16, 100) == 0        # K % 128
     assert C.chord_w4a16_packed_bytes(0, 0, 1, 24, 128) == 0        # I % 8 for gate_up
     assert C.chord_moe_align_max_padded(64, 8, 48, 16) == 512 + 48 * 15
-    assert C.chord_w4a16_moe_indexed_block_m(64, 8, 384, 48, 7168, 2048) in (16, 32, 64, 128)
+    # decode: routed inside the GEMM, no alignment (block_m 0); prefill aligns
+    assert C.chord_w4a16_moe_indexed_block_m(64, 8, 384, 48, 7168, 2048) == 0
+    assert C.chord_w4a16_moe_indexed_block_m(8192, 8, 384, 48, 7168, 2048) in (16, 32, 64, 128)
 
 
 def _handle(mode, role, E=2, N=256, K=256):
@@ -75,11 +77,19 @@ def test_layer_rejects_wrong_mode_and_role():
     assert _indexed(_handle(0, 1), _handle(0, 1, N=256, K=128)) == 3      # role mismatch
 
 
+def _aligned():
+    # a kernel-1 override keeps a small call on the alignment (not routed)
+    s = C.Schedule()
+    s.kernel = 1
+    return s
+
+
 def test_layer_host_validation():
     h13, h2 = _handle(0, 0), _handle(0, 1, N=256, K=128)
+    ov = _aligned()
     assert _indexed(h13, h2, null_x=True) == 1
-    assert _indexed(h13, h2, bm=24) == 1
-    assert _indexed(h13, h2, max_padded=3) == 1
+    assert _indexed(h13, h2, bm=24, ov=ctypes.byref(ov)) == 1
+    assert _indexed(h13, h2, max_padded=3, ov=ctypes.byref(ov)) == 1
     assert _indexed(h13, h2, ws=16) == 4
     assert _indexed(h13, h2, I=64) == 1                                   # shape mismatch with handle
     bad = C.Schedule()
@@ -184,8 +194,9 @@ def test_noalloc_entry_point_rejects_misuse_and_oversize_calls_on_the_host():
     whose scratch would exceed CHORD_NOALLOC_SCRATCH_BYTES (64 MiB) is
     refused before anything touches the device."""
     h13, h2 = _handle(0, 0), _handle(0, 1, N=256, K=128)
-    assert _indexed_noalloc(h13, h2, bm=24) == 1
-    assert _indexed_noalloc(h13, h2, max_padded=3) == 1
+    ov = _aligned()
+    assert _indexed_noalloc(h13, h2, bm=24, ov=ctypes.byref(ov)) == 1
+    assert _indexed_noalloc(h13, h2, max_padded=3, ov=ctypes.byref(ov)) == 1
     assert _indexed_noalloc(_handle(1, 0), h2) == 3
     three = C.Schedule()
     three.kernel = 3
@@ -200,3 +211,21 @@ def test_noalloc_entry_point_rejects_misuse_and_oversize_calls_on_the_host():
     assert need > 64 << 20
     assert _indexed_noalloc(g13, g2, T=8192, H=7168, I=2048, k=8) == 4
     assert b"scratch" in C.lib.chord_last_error()
+
+
+def test_routed_call_reads_no_alignment():
+    """A small indexed call is routed inside the GEMM: null alignment
+    pointers pass host validation (the call then stops at the device check,
+    CHORD_ERR_HIP here without a GPU), while an aligned schedule override
+    still requires them."""
+    h13, h2 = _handle(0, 0, N=256, K=384), _handle(0, 1, N=384, K=128)
+    assert C.chord_w4a16_moe_indexed_block_m(4, 2, 8, 2, 384, 128) == 0
+    r = C.lib.chord_w4a16_moe_indexed(FAKE, 4, 384, 128, ctypes.byref(h13), ctypes.byref(h2),
+                                      FAKE, FAKE, 2, 0, 8, None, None, None, 0, 0, FAKE, FAKE,
+                                      1 << 30, None, 0, None)
+    assert r == 6, C.lib.chord_last_error()
+    ov = _aligned()
+    r = C.lib.chord_w4a16_moe_indexed(FAKE, 4, 384, 128, ctypes.byref(h13), ctypes.byref(h2),
+                                      FAKE, FAKE, 2, 0, 8, None, None, None, 0, 0, FAKE, FAKE,
+                                      1 << 30, ctypes.byref(ov), 0, None)
+    assert r == 1 and b"alignment" in C.lib.chord_last_error()

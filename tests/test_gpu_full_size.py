@@ -41,9 +41,12 @@ def _run_indexed(C, wl):
     from quantized_moe_amd.moe import W4A16MoE
     layer = W4A16MoE(dev(wl.q13), dev_bf16(wl.s13), dev(wl.q2), dev_bf16(wl.s2))
     bm = C.chord_w4a16_moe_indexed_block_m(wl.T, wl.k, wl.E_g, wl.E_l, wl.H, wl.I)
-    mp = C.chord_moe_align_max_padded(wl.T, wl.k, wl.E_l, bm)
     ids = dev(wl.topk_ids)
-    al = C.chord_moe_align(ids, wl.expert_begin, wl.E_l, bm, max_padded=mp)
+    if bm:
+        mp = C.chord_moe_align_max_padded(wl.T, wl.k, wl.E_l, bm)
+        al = C.chord_moe_align(ids, wl.expert_begin, wl.E_l, bm, max_padded=mp)
+    else:                                # routed inside the GEMM: no alignment
+        al = (None, None, None)
     out = layer.indexed(dev_bf16(wl.x), ids, dev(wl.topk_weights), wl.expert_begin, wl.E_g,
                         align=(*al, bm))
     torch.cuda.synchronize()

@@ -460,3 +460,138 @@ def test_tile_k_split_of_a_hot_expert_is_deterministic_and_close():
         sl = slice(e * max_m, e * max_m + mm[e])
         assert np.array_equal(outs[0][sl], outs[1][sl]) and np.array_equal(outs[0][sl], outs[2][sl])
         check_close(outs[0][sl], ref[sl], f"masked e={e}")
+
+
+# ---------------------------------------------------------------------------
+# routed calls: rows from topk_ids inside the gate_up launch (no alignment)
+# ---------------------------------------------------------------------------
+
+def run_routed(x, ids, w, q13, s13, q2, s2, eb, E_g, layer=None, flags=0):
+    """The planner's own choice with no alignment (block_m 0)."""
+    from quantized_moe_amd.moe import W4A16MoE
+    if layer is None:
+        layer = W4A16MoE(dev(q13), dev_bf16(s13), dev(q2), dev_bf16(s2))
+    T, k = ids.shape
+    E_l, H, I = q13.shape[0], x.shape[1], q2.shape[2] * 8
+    assert C.chord_w4a16_moe_indexed_block_m(T, k, E_g, E_l, H, I) == 0
+    out = layer.indexed(dev_bf16(x), dev(ids), dev(w), expert_begin=eb, num_global_experts=E_g,
+                        block_m=0, flags=flags)
+    torch.cuda.synchronize()
+    return host_bf16(out), layer
+
+
+@pytest.mark.parametrize("T,H,I,E_g,E_l,k,eb", [
+    (64, 1024, 512, 64, 16, 8, 8),      # decode-like: ~1 row per expert, non-local slots
+    (160, 512, 512, 64, 24, 8, 0),      # ~20 rows per expert: 32-row token tiles
+    (300, 640, 256, 384, 384, 2, 0),    # TP-like, short-K down GEMM
+    (256, 384, 384, 384, 64, 8, 0),     # 2048 slots, the routed maximum
+])
+def test_routed_equals_aligned_bit_identical(T, H, I, E_g, E_l, k, eb):
+    """A routed call and the same schedule on the alignment (kernel-1
+    override) compute every row from the same chunks in the same order, so
+    they agree bit for bit; the rows of an expert may share tiles in another
+    order, which changes no row."""
+    banner(f"routed vs aligned T={T} H={H} I={I} E_g={E_g} E_l={E_l} k={k}")
+    case = small_case(T * 13 + I, T, H, I, E_g, E_l, k, eb)
+    routed, layer = run_routed(*case, E_g=E_g)
+    plan = C.last_plan()
+    assert "tiles=routed" in plan and "down+combine" not in plan, plan
+    aligned, _, _ = run_indexed(*case, E_g=E_g, bm=16, layer=layer, override={"kernel": 1})
+    assert "tiles=blocks" in C.last_plan() or "tiles=list" in C.last_plan()
+    assert np.array_equal(routed, aligned)
+    check_close(routed, oracle.moe_layer(*case))
+    again, _ = run_routed(*case, E_g=E_g, layer=layer)
+    assert np.array_equal(again, routed)
+
+
+def test_routed_hot_experts_span_many_tiles():
+    """Skewed routing: hot experts hold up to ~150 rows, i.e. several 16-row
+    tiles of one routed expert."""
+    banner("routed: skewed experts over many tiles")
+    case = skewed_case(78, 300, 512, 512, 64, 2, [60, 30, 20] + [1] * 61)
+    counts = np.bincount(case[1].ravel(), minlength=64)
+    assert counts.max() > 64, counts.max()
+    routed, layer = run_routed(*case, E_g=64)
+    assert "tiles=routed" in C.last_plan()
+    aligned, _, _ = run_indexed(*case, E_g=64, bm=16, layer=layer, override={"kernel": 1})
+    assert np.array_equal(routed, aligned)
+    check_close(routed, oracle.moe_layer(*case))
+
+
+def test_routed_validate_flag_and_no_local_slot():
+    banner("routed: validate flag, tokens without a local slot")
+    case = small_case(79, 40, 512, 512, 128, 16, 4, expert_begin=100)
+    x, ids, w, *rest = case
+    got, _ = run_routed(x, ids, w, *rest, E_g=128, flags=C.FLAG_VALIDATE)
+    ref = oracle.moe_layer(x, ids, w, *rest)
+    check_close(got, ref)
+    none = ~np.any((ids >= 100) & (ids < 116), axis=1)
+    assert none.any() and np.all(got[none] == 0)
+
+
+@pytest.mark.parametrize("T,H,I,E_g,E_l,k,eb", [
+    (1, 1024, 256, 384, 384, 8, 0),     # the single-token TP slice, small H
+    (2, 512, 512, 64, 16, 8, 4),        # some slots non-local
+    (16, 384, 128, 16, 16, 4, 0),       # 64 slots, 16 tokens: the fused maximum
+    (5, 384, 256, 32, 32, 1, 0),        # top-1
+    (3, 384, 128, 64, 4, 8, 60),        # likely tokens without a local slot
+])
+def test_fused_down_combine_matches_the_oracle(T, H, I, E_g, E_l, k, eb):
+    """T <= 16 and T*k <= 64: the down GEMM and the combine run as one launch
+    that sums w * y in fp32 without rounding y first (the oracle's reading);
+    the aligned path rounds y to bf16 before its combine, so the two agree
+    within the tolerance, not bit for bit."""
+    banner(f"fused down+combine T={T} H={H} I={I} E_g={E_g} E_l={E_l} k={k} eb={eb}")
+    case = small_case(T * 17 + H + k, T, H, I, E_g, E_l, k, eb)
+    fused, layer = run_routed(*case, E_g=E_g)
+    assert "down+combine" in C.last_plan(), C.last_plan()
+    ref = oracle.moe_layer(*case)
+    st = check_close(fused, ref, "fused")
+    banner(f"  {st}")
+    aligned, _, _ = run_indexed(*case, E_g=E_g, bm=16, layer=layer, override={"kernel": 1})
+    check_close(fused, aligned, "fused vs aligned")
+    ids = case[1]
+    none = ~np.any((ids >= eb) & (ids < eb + E_l), axis=1)
+    assert np.all(fused[none] == 0)
+    again, _ = run_routed(*case, E_g=E_g, layer=layer)
+    assert np.array_equal(again, fused)
+
+
+@pytest.mark.parametrize("T,k", [(12, 4), (64, 8)])
+def test_routed_layer_replays_in_a_hip_graph(T, k):
+    """A routed call (no alignment launch; fused down+combine at T = 12)
+    captured in a HIP graph and replayed on new inputs in the same buffers:
+    every replay equals an eager call bit for bit."""
+    from quantized_moe_amd.moe import W4A16MoE
+    banner(f"graph replay, routed T={T} k={k}")
+    H, I, E_g, E_l = 512, 512, 64, 16
+    base = small_case(800 + T, T, H, I, E_g, E_l, k)
+    layer = W4A16MoE(dev(base[3]), dev_bf16(base[4]), dev(base[5]), dev_bf16(base[6]))
+    x, ids, w = dev_bf16(base[0]), dev(base[1]), dev(base[2])
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def step(o):
+        layer.indexed(x, ids, w, 0, E_g, block_m=0, out=o)
+
+    step(out)
+    torch.cuda.synchronize()
+    assert "tiles=routed" in C.last_plan()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        case = small_case(900 + r, T, H, I, E_g, E_l, k)
+        x.copy_(dev_bf16(case[0]))
+        ids.copy_(dev(case[1]))
+        w.copy_(dev(case[2]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = host_bf16(out)
+        eager_out = torch.empty_like(out)
+        step(eager_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(replayed, host_bf16(eager_out)), f"replay {r}"
+        check_close(replayed, oracle.moe_layer(case[0], case[1], case[2], base[3], base[4],
+                                               base[5], base[6], 0), f"replay {r}")

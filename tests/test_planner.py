@@ -124,3 +124,15 @@ for i in range(60):
     assert r.returncode == 0, r.stderr
     lines = [l for l in r.stderr.splitlines() if l.startswith("[chord] plan")]
     assert len(lines) == 3, lines
+
+
+def test_routed_calls_need_a_gate_up_k_over_two_chunks():
+    """Routed calls (no alignment) need the general streaming kernel for the
+    gate_up: at H <= 256 the short-K variant would run, which reads its tiles
+    from the alignment, so such calls align."""
+    assert C.chord_w4a16_moe_indexed_block_m(256, 8, 384, 64, 256, 384) != 0
+    assert C.chord_w4a16_moe_indexed_block_m(256, 8, 384, 64, 384, 384) == 0
+    assert "tiles=routed" not in C.chord_w4a16_moe_plan(C.MODE_INDEXED, 256, 8, 384, 64, 256, 384,
+                                                       0, 0)
+    assert "tiles=routed" in C.chord_w4a16_moe_plan(C.MODE_INDEXED, 256, 8, 384, 64, 384, 384, 0,
+                                                   0)
