@@ -103,7 +103,12 @@ typedef struct {
                           then ignored), 3 both: experts with >= 48 rows take the
                           tiled GEMMs (on an internal side stream, joined back
                           to the caller's stream), the others the streaming
-                          GEMMs */
+                          GEMMs; 4 / 5: the LDS-tiled GEMMs in their single-role
+                          form (every wave dequantises and multiplies) / their
+                          producer-consumer form (K > 256: 8 waves only issue
+                          MFMAs on LDS operands, 4 waves load and dequantise;
+                          tiles of up to 176 rows), where kernel 2 lets the
+                          planner choose; both forms give bit-identical results */
   int32_t tokens;      /* rows per token tile of kernel 1: 16 or 32; 0 auto */
   int32_t gate_up_nt;  /* 16-row weight tiles per wave in the gate_up GEMM: 2 or 4; 0 auto */
   int32_t gate_up_wk;  /* waves splitting K in the gate_up GEMM: 1, 2 or 4; 0 auto */

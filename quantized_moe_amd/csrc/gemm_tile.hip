@@ -436,6 +436,289 @@ __global__ __launch_bounds__(64 * W) void gemm_tile(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Producer/consumer form (K > 256, no K split): the dequantisation moves out
+// of the MFMA waves.  On gfx950 VALU work that other waves issue overlaps a
+// wave's back-to-back MFMAs almost entirely, while the same work interleaved
+// in the MFMA wave's own stream slows it by a fifth to a third (measured with
+// a timing probe at 1 to 2 dequantised words per 16 MFMAs), so a workgroup of
+// 12 waves splits into:
+//   * 8 consumers (two per SIMD) owning 2 weight tiles (32 output rows)
+//     each: per MFMA step they read their dequantised A fragments and the
+//     token B fragments from LDS and issue 2 x MG MFMAs;
+//   * 4 producers (one per SIMD) owning 4 tiles each: they stream the packed
+//     weights into registers two chunks ahead, dequantise each step two steps
+//     ahead of the consumers into a 3-stage LDS ring of bf16 A fragments
+//     (16 KB per step: 16 tiles x 64 lanes x 16 B, each lane's fragment where
+//     the consumer lane of the same index reads it), and DMA the token chunk
+//     one chunk ahead into 2 stages.
+// One workgroup barrier per step; both roles pass the same number.  Every
+// output is summed over the same chunks and steps in the same order as in
+// run_item, so both forms agree bit for bit.
+//
+// Measured on the prefill EP share it is the slower form (gate_up 542 vs
+// 400 us): with the producers' dequantisation switched off (timing only) the
+// consumers alone take 376 us, so the A fragments' round trip through LDS and
+// the per-step barriers cost nearly all that the overlap gains.  The planner
+// therefore keeps the single-role form; this one is opt-in (schedule kernel 5,
+// CHORD_W4A16_TILE_PC=1).
+// ---------------------------------------------------------------------------
+constexpr int kPcWaves = 12;
+constexpr int kPcConsumers = 8;
+constexpr int kPcXStages = 2;
+constexpr int kPcAStages = 3;
+constexpr int kPcAStepBytes = kSliceTiles * 64 * 16;
+constexpr size_t kPcLdsBytes = kPcXStages * (size_t)kXBufBytes +
+                               kPcAStages * (size_t)kPcAStepBytes + kMaxGroups * 16 * (4 + 8 + 4);
+
+// Workgroup barrier of the producer/consumer form: wait for this wave's own
+// counters (an s_waitcnt immediate), then s_barrier.  The empty asm with a
+// memory clobber on both sides keeps the compiler from moving or merging LDS
+// accesses across it (s_barrier alone is not a memory operation to the
+// compiler), and the scheduling fences keep the machine scheduler out.
+template <int kWait>
+__device__ __forceinline__ void pc_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWait);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// s_waitcnt immediates (gfx9 encoding): LDS done and no vector-memory wait;
+// LDS done and at most N vector-memory operations in flight.
+constexpr int kWaitLds = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+template <int N>
+constexpr int wait_vm_lds() { return (N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14); }
+
+template <int MG>
+__device__ __forceinline__ void run_item_pc(const GemmArgs& a, uint8_t* xbuf, uint8_t* abuf,
+                                            const int32_t* srcoff, const int64_t* dstrow,
+                                            const float* roww, const TileDesc& td, int ng) {
+  constexpr int NTC = kSliceTiles / kPcConsumers;                   // 2 tiles per consumer
+  constexpr int NTP = kSliceTiles / (kPcWaves - kPcConsumers);      // 4 tiles per producer
+  constexpr int kDma = MG;    // token DMA instructions per producer and chunk (4 MG row blocks)
+  constexpr int kWLoads = 2 * NTP;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4;
+  const int col = lane & 15;
+  const int nc = a.n_chunks;  // > 2 here
+  const int e = td.expert;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  // Lane l's 16-byte A fragment of slice tile t in stage st of the ring.
+  auto afrag = [&](int stage, int t) {
+    return abuf + stage * kPcAStepBytes + (t * 64 + lane) * 16;
+  };
+
+  if (wave >= kPcConsumers) {
+    // ------------------------------ producer ------------------------------
+    const int pw = wave - kPcConsumers;
+    const int ptile0 = ng * kSliceTiles + pw * NTP;
+    const int tile_ld = ptile0 + NTP <= a.n_tiles ? ptile0 : a.n_tiles - NTP;  // past the end: re-read
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
+    uint32_t voff[kDma];
+    int jblk[kDma];
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+      jblk[i] = pw + 4 * i;  // row blocks 4 jblk .. 4 jblk + 3 (all < 4 MG)
+      const int row = 4 * jblk[i] + q;
+      voff[i] = (uint32_t)srcoff[row] + (uint32_t)((col ^ swz(row & 15)) * 16);
+    }
+    auto dma_x = [&](int c) {  // token chunk c into stage c % 2
+#pragma unroll
+      for (int i = 0; i < kDma; ++i) {
+        uint8_t* dst = xbuf + (c & 1) * kXBufBytes + jblk[i] * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, (__attribute__((address_space(3))) void*)dst, 16, voff[i], c * kChunkK * 2, 0, 0);
+      }
+    };
+    const int64_t expert_bytes = (int64_t)a.n_tiles * nc * kBlockBytes;
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+    uint4 wq[3][NTP];
+    uint32_t sc[3][NTP];
+    auto load_w = [&](int slot, int c) {
+#pragma unroll
+      for (int nt = 0; nt < NTP; ++nt) {
+        const uint32_t blk = (uint32_t)((tile_ld + nt) * nc + c) * kBlockBytes;
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+        wq[slot][nt] = make_uint4(v[0], v[1], v[2], v[3]);
+        sc[slot][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+      }
+    };
+    // Dequantise MFMA step st of the chunk in weight slot `slot` into stage
+    // `stage` of the A ring (tiles of a clamped re-read land in the slots of
+    // the slice's last tiles with the same values, or past n_tiles where no
+    // consumer reads them).
+    auto produce = [&](int slot, int st, int stage) {
+#pragma unroll
+      for (int nt = 0; nt < NTP; ++nt) {
+        const bf16x8_t w = dequant_word(word_of(wq[slot][nt], st), dq_scale(sc[slot][nt]));
+        *reinterpret_cast<bf16x8_t*>(afrag(stage, pw * NTP + nt)) = w;
+      }
+    };
+    dma_x(0);
+    load_w(0, 0);
+    load_w(1, 1);
+    produce(0, 0, 0);
+    produce(0, 1, 1);
+    // x(0) landed (only w(1) may still be in flight), A stages 0 and 1 written
+    pc_barrier<wait_vm_lds<kWLoads>()>();
+    // Chunk c in weight slot cs = c % 3.  Step st dequantises step 4c + st + 2
+    // into ring stage (4c + st + 2) % 3 = (cs + st + 2) % 3.
+    auto chunk = [&](int cs, int c) {
+      if (c >= nc) return;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st == 0) {
+          dma_x(c + 1 < nc ? c + 1 : nc - 1);                     // into the stage chunk c-1 used
+          load_w((cs + 2) % 3, c + 2 < nc ? c + 2 : nc - 1);      // into the slot chunk c-1 used
+        }
+        if (4 * c + st + 2 < 4 * nc) {
+          if (st < 2) produce(cs, st + 2, (cs + st + 2) % 3);
+          else produce((cs + 1) % 3, st - 2, (cs + st + 2) % 3);
+        }
+        if (st == 3)
+          pc_barrier<wait_vm_lds<kWLoads>()>();  // x(c+1) landed: only w(c+2) may be in flight
+        else
+          pc_barrier<kWaitLds>();                // A writes done
+      }
+    };
+    for (int c = 0; c < nc; c += 3) {
+      chunk(0, c);
+      chunk(1, c + 1);
+      chunk(2, c + 2);
+    }
+    // drain everything (the clamped prefetches) before the next item
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  // ------------------------------ consumer ------------------------------
+  const int tile0 = ng * kSliceTiles + wave * NTC;
+  const bool live = tile0 < a.n_tiles;
+  f32x4_t acc[NTC][MG];
+#pragma unroll
+  for (int nt = 0; nt < NTC; ++nt)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[nt][g] = zero4;
+  uint32_t boff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    boff[st] = (uint32_t)(col * 256 + (((q * 4 + st) ^ swz(col)) * 16));
+  auto bread = [&](const uint8_t* xb, int st, int g) {
+    return *reinterpret_cast<const bf16x8_t*>(xb + boff[st] + g * 16 * 256);
+  };
+  auto aread = [&](int stage, bf16x8_t (&av)[NTC]) {
+#pragma unroll
+    for (int nt = 0; nt < NTC; ++nt)
+      av[nt] = *reinterpret_cast<const bf16x8_t*>(afrag(stage, wave * NTC + nt));
+  };
+  pc_barrier<kWaitLds>();  // the producers' prologue
+  bf16x8_t av[NTC], an[NTC];
+  aread(0, av);
+  // Step 4c + st reads ring stage (4c + st) % 3; the next step's A (written
+  // a step ago) is read during this step, ahead of its use.
+  int stage = 0;  // (4c) % 3
+  for (int c = 0; c < nc; ++c) {
+    const uint8_t* xb = xbuf + (c & 1) * kXBufBytes;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int next = stage == 2 ? 0 : stage + 1;
+      if (4 * c + st + 1 < 4 * nc) aread(next, an);
+      bf16x8_t bwin[3];
+      bwin[0] = bread(xb, st, 0);
+      if (MG > 1) bwin[1] = bread(xb, st, 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < MG; ++g) {
+        if (g + 2 < MG) bwin[(g + 2) % 3] = bread(xb, st, g + 2);
+        const bf16x8_t bv = bwin[g % 3];
+#pragma unroll
+        for (int nt = 0; nt < NTC; ++nt)
+          acc[nt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nt], bv, acc[nt][g], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keep the B reads two groups ahead, no further
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTC; ++nt) av[nt] = an[nt];
+      stage = next;
+      pc_barrier<kWaitLds>();  // this step's LDS reads done
+    }
+  }
+  if (!live) return;
+  if (!a.gate_up) {
+    store_down_pairs<NTC, MG>(a, acc, dstrow, roww, tile0, q, col);
+    return;
+  }
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    const int64_t dr = dstrow[g * 16 + col];
+#pragma unroll
+    for (int nt = 0; nt < NTC; ++nt) {
+      if (dr < 0) continue;
+      const f32x4_t v = acc[nt][g];
+      const int f0 = (tile0 + nt) * 8 + 2 * q;
+      *reinterpret_cast<uint32_t*>(a.out + dr * (int64_t)a.out_ld + f0) =
+          pk_bf16(silu_mul(v[0], v[1]), silu_mul(v[2], v[3]));
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * kPcWaves) void gemm_tile_pc(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* xbuf = smem;                                                   // [2][192][256 B]
+  uint8_t* abuf = smem + kPcXStages * kXBufBytes;                         // [3][16][64][16 B]
+  int32_t* srcoff = reinterpret_cast<int32_t*>(abuf + kPcAStages * kPcAStepBytes);  // [192]
+  int64_t* dstrow = reinterpret_cast<int64_t*>(srcoff + kMaxGroups * 16);           // [192]
+  float* roww = reinterpret_cast<float*>(dstrow + kMaxGroups * 16);                 // [192]
+  const int tid = threadIdx.x;
+  const int nslices = a.items_per_tile;
+  // XCD-aware item order as in gemm_tile.
+  const int G = gridDim.x < kXcds ? (int)gridDim.x : kXcds;
+  const int xg = blockIdx.x % G;
+  const int nloc = (gridDim.x + G - 1 - xg) / G;
+  const int lidx = blockIdx.x / G;
+  for (int g = xg; g < kTileGroups; g += G)
+    for (int j = lidx, t0 = a.status->group_start[g],
+             n_items = (a.status->group_start[g + 1] - t0) * nslices;
+         j < n_items; j += nloc) {
+      const TileDesc td = a.tiles[t0 + j / nslices];
+      const int ng = j % nslices;
+      const int e = td.expert;
+      const int nrows = td.nrows < kMaxGroups * 16 ? td.nrows : kMaxGroups * 16;
+      if (tid < kMaxGroups * 16) {
+        const int m = tid;
+        int32_t so = (int32_t)kNoRow;
+        int64_t dr = -1;
+        if (m < nrows) {
+          const RowMap rm = map_row(a, e, (int64_t)td.row_begin + m);
+          if (rm.src >= 0) {
+            so = (int32_t)(rm.src * (int64_t)a.K * 2);
+            dr = rm.dst;
+          }
+        }
+        srcoff[m] = so;
+        dstrow[m] = dr;
+        roww[m] = (dr >= 0 && !a.gate_up && a.row_weights != nullptr) ? a.row_weights[dr] : 1.0f;
+      }
+      __syncthreads();
+      switch ((nrows + 15) >> 4) {
+        case 0: break;
+#define CHORD_PC_CASE(MG) \
+  case MG: run_item_pc<MG>(a, xbuf, abuf, srcoff, dstrow, roww, td, ng); break;
+        CHORD_PC_CASE(1) CHORD_PC_CASE(2) CHORD_PC_CASE(3) CHORD_PC_CASE(4)
+        CHORD_PC_CASE(5) CHORD_PC_CASE(6) CHORD_PC_CASE(7) CHORD_PC_CASE(8)
+        CHORD_PC_CASE(9) CHORD_PC_CASE(10) CHORD_PC_CASE(11)
+#undef CHORD_PC_CASE
+        default: run_item_pc<12>(a, xbuf, abuf, srcoff, dstrow, roww, td, ng); break;
+      }
+      __syncthreads();  // row maps, token stages and A ring reused by the next item
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Short-K variant (K <= 256, e.g. the down GEMM of an 8-way intermediate
 // split): the whole token tile (all K) is staged in LDS once per work item,
 // and the item covers `slices_per_item` consecutive 256-row slices.  The
@@ -733,6 +1016,16 @@ hipError_t launch_gemm_tile(const GemmArgs& a, int grid, hipStream_t stream) {
     return hipGetLastError();
   }
   const int cus = a.num_cus > 0 ? a.num_cus : 256;
+  if (a.tile_waves == 2) {  // producer/consumer form (no K split)
+    static const int per_cu_pc = [] {
+      hipFuncSetAttribute((const void*)gemm_tile_pc, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kPcLdsBytes);
+      return blocks_per_cu(gemm_tile_pc, 64 * kPcWaves, kPcLdsBytes);
+    }();
+    if (grid > per_cu_pc * cus) grid = per_cu_pc * cus;
+    hipLaunchKernelGGL(gemm_tile_pc, dim3(grid), dim3(64 * kPcWaves), kPcLdsBytes, stream, a);
+    return hipGetLastError();
+  }
   if (a.tile_waves == 8) {
     static const int per_cu8 = [] {
       hipFuncSetAttribute((const void*)gemm_tile<8>, hipFuncAttributeMaxDynamicSharedMemorySize,

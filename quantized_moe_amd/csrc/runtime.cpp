@@ -89,6 +89,7 @@ struct EnvOverrides {
   int gu_nt = 0, gu_wk = 0, dn_nt = 0, dn_wk = 0;  // "nt,wk" per GEMM
   int tile_wgs = 0;  // tiled kernel: workgroups per CU
   int tile_waves = 0;  // tiled kernel (K > 256): waves per workgroup, 4 or 8
+  int tile_pc = 0;     // tiled kernel (K > 256): 1 producer/consumer form, 0 off
   int tile_split = 0;  // tiled kernel: 1 turns the K split of outsized tiles off
   int stream_wgs = 0;  // streaming kernel: workgroups per CU (0: balanced default)
   int prefetch = 0;
@@ -104,6 +105,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_DOWN")) sscanf(s, "%d,%d", &o.dn_nt, &o.dn_wk);
     if (const char* s = getenv("CHORD_W4A16_TILE_WGS")) o.tile_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_TILE_WAVES")) o.tile_waves = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_TILE_PC")) o.tile_pc = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_TILE_SPLIT")) o.tile_split = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_STREAM_WGS")) o.stream_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
@@ -182,6 +184,8 @@ struct Plan {
   int max_tiles_b;   // big-tile list capacity
   int split_rows;    // kernel 3: experts with >= split_rows rows take the tiled kernel
   bool tile_ksplit;  // tiled kernel: outsized tiles may be split along K
+  bool tile_pc;      // tiled GEMMs with K > 256 in the producer/consumer form
+  int big_tokens;    // rows per big tile
   bool routed;       // indexed: rows from topk_ids inside the gate_up launch (no alignment read)
   bool fused;        // routed: down GEMM and combine in one launch
   int cus;
@@ -194,6 +198,8 @@ std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 
 constexpr int kTileSlice = 256;    // output rows per workgroup of the tiled kernel
 constexpr int kTileTokens = 192;   // token rows per big tile (tiled kernel)
+constexpr int kTileTokensPc = 176; // ... in the producer/consumer form (11 token groups)
+constexpr double kPcMinRows = 64.0;  // producer/consumer form from this many rows per expert
 constexpr double kTileMinRows = 24.0;        // auto choice of the tiled family
 constexpr double kTileMinRowsShortK = 8.0;   // same, when the down GEMM is short-K
 constexpr double kSplitRows = 48.0;          // kernel 3: experts with this many rows go tiled
@@ -221,6 +227,13 @@ Plan make_plan(const PlanKey& key) {
   p.cus = key.cus;
   const bool tile_ok = (2 * key.I) % 64 == 0 && key.H % 64 == 0;  // 4 tiles per wave
   int kernel = key.ov[0] ? key.ov[0] : env().kernel;
+  // Kernel 4 / 5: the LDS-tiled family in its single-role / producer-
+  // consumer form (kernel 2 lets the planner choose the form).
+  int tile_form = 0;  // 0 planner, 1 single-role, 2 producer/consumer
+  if (kernel == 4 || kernel == 5) {
+    tile_form = kernel - 3;
+    kernel = 2;
+  }
   if (kernel < 1 || kernel > 3) {
     // Expected rows per expert decide the family (measured crossovers on
     // MI355X at steady clocks): the tiled kernel from 24 rows, or from 8 when
@@ -236,7 +249,7 @@ Plan make_plan(const PlanKey& key) {
   if (!tile_ok) kernel = 1;
   p.kernel = kernel;
   p.split_rows = kernel == 3 ? (int)kSplitRows : (kernel == 2 ? 0 : INT32_MAX);
-  p.max_tiles_b = kernel & 2 ? max_tiles_for(key.rows, key.E_l, kTileTokens) : 0;
+  p.max_tiles_b = kernel & 2 ? max_tiles_for(key.rows, key.E_l, kTileTokensPc) : 0;
   // K split of outsized big tiles (masked layout: budgets per expert with
   // skewed counts): both tiled GEMMs must run the general tiled kernel
   // (K > 256; the short-K kernel has no split), and no override or
@@ -245,6 +258,13 @@ Plan make_plan(const PlanKey& key) {
   // (The workspace holds partial slots for masked calls only.)
   p.tile_ksplit = (kernel & 2) && key.mode == kMasked && key.H / kChunkK > 2 &&
                   key.I / kChunkK > 2 && key.ov[7] != 1 && env().tile_split != 1;
+  // Producer/consumer form of the tiled GEMMs with K > 256: waves that only
+  // issue MFMAs and waves that only load and dequantise (no K split; tiles of
+  // at most 176 rows).  It pays once tiles hold many token groups.
+  if (tile_form == 0)
+    tile_form = (env().tile_pc == 1 && tok_e >= kPcMinRows) ? 2 : 1;
+  p.tile_pc = kernel == 2 && tile_form == 2 && !p.tile_ksplit;
+  p.big_tokens = p.tile_pc ? kTileTokensPc : kTileTokens;
 
   // Tiled GEMMs: one workgroup per CU (registers, ~150 KB of LDS); the
   // launcher clamps to the occupancy it measures.
@@ -262,8 +282,10 @@ Plan make_plan(const PlanKey& key) {
     }
     g.slices = S;
     // Two waves per SIMD (8 per workgroup, 2 weight tiles each): one wave
-    // cannot keep the MFMA pipe busy (prefill gate_up 486 -> 434 us).
+    // cannot keep the MFMA pipe busy (prefill gate_up 486 -> 434 us).  Or
+    // the producer/consumer form (marked waves = 2).
     g.waves = env().tile_waves == 4 ? 4 : 8;
+    if (p.tile_pc && K / kChunkK > 2) g.waves = 2;
     const int64_t items = (int64_t)p.max_tiles_b * ((nslices + S - 1) / S);
     const int per_cu = env().tile_wgs > 0 ? env().tile_wgs : 1;
     g.grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)per_cu * key.cus));
@@ -381,9 +403,11 @@ Plan make_plan(const PlanKey& key) {
                   p.dn.slices);
   n = std::min(cap, n);
   if (kernel & 2)
-    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d, %d waves (slices/item %d, %d)%s",
-             kTileTokens, p.gut.waves, p.gut.slices, p.dnt.slices,
-             kernel == 3 ? " for experts with >= 48 rows" : "");
+    snprintf(p.text + n, sizeof(p.text) - n, " | tile 256x%d, %s (slices/item %d, %d)%s",
+             p.big_tokens,
+             p.tile_pc ? (p.dnt.waves == 2 ? "producer/consumer" : "producer/consumer gate_up")
+                       : (p.gut.waves == 4 ? "4 waves" : "8 waves"),
+             p.gut.slices, p.dnt.slices, kernel == 3 ? " for experts with >= 48 rows" : "");
   return p;
 }
 
@@ -467,7 +491,7 @@ WsLayout layer_ws(int mode, int T, int k, int E_l, int H, int I, int64_t rows) {
   rows = std::max(rows, slots);
   w.max_tiles = max_tiles_for(rows, E_l, 16);
   // Big tiles, plus up to 3 extra entries per K-split tile.
-  w.max_tiles_b = max_tiles_for(rows, E_l, kTileTokens) + 3 * kMaxSplitTiles;
+  w.max_tiles_b = max_tiles_for(rows, E_l, kTileTokensPc) + 3 * kMaxSplitTiles;
   w.max_slices = (std::max(2 * I, H) + kTileSlice - 1) / kTileSlice;
   size_t off = 0;
   w.status = off;
@@ -582,7 +606,7 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   gt.tiles = tiles_b;
   gt.tiles_per_item = kTileSlice / kTileRows;
   gt.items_per_tile = (g.n_tiles + gt.tiles_per_item - 1) / gt.tiles_per_item;
-  gt.tile_tokens = kTileTokens;
+  gt.tile_tokens = plan.big_tokens;
   gt.slices_per_item = std::max(1, std::min(tp.slices, gt.items_per_tile));
   gt.tile_waves = tp.waves;
   if (plan.kernel == 1) return launch_gemm(1, sp.nt, plan.mt, sp.wk, sp.pf, gs, sp.grid, stream);
@@ -638,7 +662,7 @@ chord_status run_expert_gemms(int layout, const Plan& plan, const WsLayout& ws, 
   tb.layout = layout;
   tb.tile_tokens = plan.tile_tokens;
   tb.max_tiles = std::min(plan.max_tiles, ws.max_tiles);
-  tb.big_tokens = kTileTokens;
+  tb.big_tokens = plan.big_tokens;
   tb.max_tiles_b = plan.tile_ksplit ? ws.max_tiles_b : std::min(plan.max_tiles_b, ws.max_tiles_b);
   tb.split_cap = plan.tile_ksplit ? kSplitCapSlots : 0;
   // Parts of at least 8 K chunks in the shorter GEMM (shorter parts spend
@@ -862,7 +886,7 @@ bool override_in_range(const chord_schedule* o) {
       if (v == x) return true;
     return false;
   };
-  return in(o->kernel, {0, 1, 2, 3}) && in(o->tokens, {0, 16, 32}) &&
+  return in(o->kernel, {0, 1, 2, 3, 4, 5}) && in(o->tokens, {0, 16, 32}) &&
          in(o->gate_up_nt, {0, 2, 4}) && in(o->down_nt, {0, 2, 4}) &&
          in(o->gate_up_wk, {0, 1, 2, 4}) && in(o->down_wk, {0, 1, 2, 4}) &&
          in(o->prefetch, {0, 2, 4}) && in(o->tile_split, {0, 1});

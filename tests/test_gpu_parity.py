@@ -595,3 +595,32 @@ def test_routed_layer_replays_in_a_hip_graph(T, k):
         assert np.array_equal(replayed, host_bf16(eager_out)), f"replay {r}"
         check_close(replayed, oracle.moe_layer(case[0], case[1], case[2], base[3], base[4],
                                                base[5], base[6], 0), f"replay {r}")
+
+
+# ---------------------------------------------------------------------------
+# producer/consumer form of the LDS-tiled GEMMs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,I,pop", [
+    (512, 384, [300, 177, 176, 100, 17, 1, 40, 64]),    # edges of the 176-row tiles
+    (640, 512, [40, 30, 20, 10, 5, 3, 2, 1]),           # skewed, ragged token groups
+])
+def test_tile_producer_consumer_form_bit_identical(H, I, pop):
+    """Kernel 5 (waves that only issue MFMAs on LDS operands, waves that only
+    load and dequantise) and kernel 4 (every wave does both) sum every output
+    over the same chunks and steps in the same order: bit-identical, whatever
+    tiles the rows fall in (176- vs 192-row tiles)."""
+    banner(f"tiled producer/consumer vs single-role H={H} I={I}")
+    E, k = len(pop), 2
+    T = sum(pop) // k + 1
+    case = skewed_case(91 + H, T, H, I, E, k, pop)
+    counts = np.bincount(case[1].ravel(), minlength=E)
+    banner(f"  rows per expert {counts.tolist()}")
+    pc, layer, _ = run_indexed(*case, E_g=E, bm=16, override={"kernel": 5})
+    assert "producer/consumer" in C.last_plan(), C.last_plan()
+    single, _, _ = run_indexed(*case, E_g=E, bm=16, layer=layer, override={"kernel": 4})
+    assert "8 waves" in C.last_plan(), C.last_plan()
+    assert np.array_equal(pc, single)
+    check_close(pc, oracle.moe_layer(*case))
+    again, _, _ = run_indexed(*case, E_g=E, bm=16, layer=layer, override={"kernel": 5})
+    assert np.array_equal(again, pc)
