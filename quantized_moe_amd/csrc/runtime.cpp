@@ -94,6 +94,7 @@ struct EnvOverrides {
   int stream_wgs = 0;  // streaming kernel: workgroups per CU (0: balanced default)
   int prefetch = 0;
   int routed = 1;  // 0: routed indexed calls off (every indexed call reads the alignment)
+  int fused = 1;   // 0: routed calls of a few tokens keep a separate combine launch
   bool log = false;
 };
 const EnvOverrides& env() {
@@ -110,6 +111,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_STREAM_WGS")) o.stream_wgs = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_ROUTED")) o.routed = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_FUSED")) o.fused = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
     return o;
   }();
@@ -308,7 +310,6 @@ Plan make_plan(const PlanKey& key) {
   p.routed = kernel == 1 && key.mode == kIndexed && key.ov[0] == 0 && env().kernel == 0 &&
              env().routed != 0 && slots >= 1 && slots <= kRoutedMaxSlots &&
              key.H / kChunkK > 2;
-  p.fused = p.routed && slots <= kFusedMaxSlots && key.T <= kFusedMaxTokens;
 
   // Streaming GEMMs.
   const double tok_small = kernel == 3 ? std::min(tok_e, kSplitRows - 1) : tok_e;
@@ -318,6 +319,10 @@ Plan make_plan(const PlanKey& key) {
   if (tokens == 16 || tokens == 32) mt = tokens / 16;
   p.mt = mt;
   p.tile_tokens = mt * 16;
+  // Fused down + combine for a handful of tokens (one launch, y never leaves
+  // the workgroup).  A down GEMM override asks for the separate down launch.
+  p.fused = p.routed && env().fused != 0 && key.ov[4] == 0 && key.ov[5] == 0 &&
+            slots <= kFusedMaxSlots && key.T <= kFusedMaxTokens;
   // key.hint carries block_m for indexed calls.
   p.block_tiles = !p.routed && kernel == 1 && key.mode == kIndexed && key.hint == p.tile_tokens;
   p.max_tiles = kernel == 2 ? 0

@@ -557,14 +557,14 @@ def test_fused_down_combine_matches_the_oracle(T, H, I, E_g, E_l, k, eb):
     assert np.array_equal(again, fused)
 
 
-@pytest.mark.parametrize("T,k", [(12, 4), (64, 8)])
-def test_routed_layer_replays_in_a_hip_graph(T, k):
+@pytest.mark.parametrize("T,k,I", [(12, 4, 512), (64, 8, 512), (48, 8, 1024)])
+def test_routed_layer_replays_in_a_hip_graph(T, k, I):
     """A routed call (no alignment launch; fused down+combine at T = 12)
     captured in a HIP graph and replayed on new inputs in the same buffers:
     every replay equals an eager call bit for bit."""
     from quantized_moe_amd.moe import W4A16MoE
-    banner(f"graph replay, routed T={T} k={k}")
-    H, I, E_g, E_l = 512, 512, 64, 16
+    banner(f"graph replay, routed T={T} k={k} I={I}")
+    H, E_g, E_l = 512, 64, 16
     base = small_case(800 + T, T, H, I, E_g, E_l, k)
     layer = W4A16MoE(dev(base[3]), dev_bf16(base[4]), dev(base[5]), dev_bf16(base[6]))
     x, ids, w = dev_bf16(base[0]), dev(base[1]), dev(base[2])

@@ -20,10 +20,22 @@ def test_decode_streams_weights_with_split_k_gate_up():
     # 64 tokens over 48 of 384 experts: about one token per expert, so every
     # GEMM streams its weights once; gate_up splits K over two waves.
     p = indexed(64, 8, 384, 48, 7168, 2048)
-    assert p.startswith("indexed: ") and "| stream " in p
+    assert p.startswith("indexed: ") and "| stream tiles=routed" in p
     assert "gate_up nt=2 wk=2" in p and "down nt=4 wk=1" in p
 
 
+@pytest.mark.parametrize("T,k,over,fused", [
+    (16, 4, None, True),                  # 64 slots, 16 tokens: the fused maximum
+    (1, 8, None, True),                   # the single-token TP slice shape
+    (17, 4, None, False),                 # 68 slots
+    (8, 8, None, True),
+    (8, 8, {"down_nt": 4}, False),        # a down override keeps the separate launches
+    (8, 8, {"gate_up_nt": 4}, True),
+])
+def test_fused_down_combine_only_for_a_handful_of_tokens(T, k, over, fused):
+    p = indexed(T, k, 384, 384, 7168, 256, override=over)
+    assert "tiles=routed" in p, p
+    assert ("down+combine" in p) == fused, p
 def test_prefill_and_large_tp_slices_take_the_tiled_kernel():
     assert "| tile 256x192" in indexed(8192, 8, 384, 48, 7168, 2048)
     for T in (512, 4096):
