@@ -295,54 +295,89 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.bsrc, 0, (int)a.bsrc_bytes, kRsrcWord3);
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int ti = item / a.items_per_tile;
-    const int ng = item % a.items_per_tile;
-    const TileDesc td = routed ? rt.tile(ti) : get_tile(a, ti);
-    const int e = td.expert;
-    if (e < 0) continue;  // uniform over the workgroup
+  // Weight and token rings, kept across items: while a wave streams the
+  // last chunks of an item it already loads the first chunks of its next
+  // item into the slots they will use (when its chunk count is a multiple of
+  // PF, so the slots line up), and that item then skips its prologue loads.
+  const int64_t expert_bytes = (int64_t)a.n_tiles * a.n_chunks * kBlockBytes;
+  const bool chain = !a.no_chain && c_hi - c_lo >= PF && (c_hi - c_lo) % PF == 0;
+  uint4 wq[PF][NT];
+  uint32_t sc[PF][NT];
+  uint4 xb[2][MT][4];
+  bool primed = false;  // the ring holds this item's first PF chunks already
 
-    // B operand: this lane supplies token `col` of each token tile, read
-    // through a bounds-checked buffer resource; lanes without a token get an
-    // out-of-range offset and read zeros (no branch around the loads).
-    uint32_t xoff[MT];
-    int64_t dst[MT];
+  // Token row offsets of tile td (lane `col` supplies token col of each
+  // 16-row token tile), and the output rows.  Lanes without a token get an
+  // out-of-range offset and read zeros (no branch around the loads).
+  auto row_maps = [&](const TileDesc& td, uint32_t (&xo)[MT], int64_t (&dr)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + col;
-      xoff[mt] = kNoRow;
-      dst[mt] = -1;
+      xo[mt] = kNoRow;
+      dr[mt] = -1;
       if (m < td.nrows) {
         RowMap rm;
         if (routed) {  // gate_up of a routed call: h row per flat slot
           const int f = rt.list[td.row_begin + m];
           rm = RowMap{f / a.topk, f};
         } else {
-          rm = map_row(a, e, (int64_t)td.row_begin + m);
+          rm = map_row(a, td.expert, (int64_t)td.row_begin + m);
         }
         if (rm.src >= 0) {
-          xoff[mt] = (uint32_t)((rm.src * (int64_t)a.K + q * kGroup) * 2);
-          dst[mt] = rm.dst;
+          xo[mt] = (uint32_t)((rm.src * (int64_t)a.K + q * kGroup) * 2);
+          dr[mt] = rm.dst;
         }
       }
     }
+  };
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int ti = item / a.items_per_tile;
+    const int ng = item % a.items_per_tile;
+    const TileDesc td = routed ? rt.tile(ti) : get_tile(a, ti);
+    const int e = td.expert;
+    if (e < 0) {  // uniform over the workgroup
+      primed = false;
+      continue;
+    }
+
+    // B operand rows of this item.
+    uint32_t xoff[MT];
+    int64_t dst[MT];
+    row_maps(td, xoff, dst);
 
     // Weights: one resource over this expert's packed tiles; the chunk and
     // tile offsets are scalar.
-    const int64_t expert_bytes = (int64_t)a.n_tiles * a.n_chunks * kBlockBytes;
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.wpack + (int64_t)e * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
     const uint32_t tile0 = (uint32_t)(ng * NT) * a.n_chunks * kBlockBytes;
+
+    // The next item of this workgroup, when the ring can run on into it.
+    bool nvalid = false;
+    __amdgpu_buffer_rsrc_t wres_n = wres;
+    uint32_t tile0_n = tile0;
+    uint32_t xoff_n[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xoff_n[mt] = xoff[mt];
+    if (chain && item + (int)gridDim.x < n_items) {
+      const int item_n = item + (int)gridDim.x;
+      const TileDesc tn = routed ? rt.tile(item_n / a.items_per_tile)
+                                 : get_tile(a, item_n / a.items_per_tile);
+      if (tn.expert >= 0) {
+        nvalid = true;
+        wres_n = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.wpack + (int64_t)tn.expert * expert_bytes), 0, (int)expert_bytes, kRsrcWord3);
+        tile0_n = (uint32_t)((item_n % a.items_per_tile) * NT) * a.n_chunks * kBlockBytes;
+        int64_t dn[MT];
+        row_maps(tn, xoff_n, dn);
+      }
+    }
 
     f32x4_t acc[NT][MT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = zero4;
-
-    uint4 wq[PF][NT];
-    uint32_t sc[PF][NT];
-    uint4 xb[2][MT][4];
 
     auto load_w = [&](int p, int c) {
 #pragma unroll
@@ -353,31 +388,41 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
         sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
       }
     };
-    auto load_x = [&](int p, int c) {
+    // Token fragments of chunk index t of this item (t >= c_hi: chunk
+    // c_lo + t - c_hi of the next item, or the last chunk again when there
+    // is none: a redundant, in-bounds load).
+    auto load_x = [&](int p, int t) {
+      const bool cross = t >= c_hi;
+      const int c = !cross ? t : (nvalid ? c_lo + (t - c_hi) : c_hi - 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t xo = cross && nvalid ? xoff_n[mt] : xoff[mt];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const u32x4_t v =
-              __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[mt], c * kChunkK * 2 + s * 16, 0);
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xres, xo, c * kChunkK * 2 + s * 16, 0);
           xb[p][mt][s] = make_uint4(v[0], v[1], v[2], v[3]);
         }
+      }
     };
     // Chunk in weight slot p.  Once tile nt is dequantised its slot
-    // registers are free, so the load of tile nt of chunk `refill` (when
-    // do_refill)
+    // registers are free, so the load of tile nt of chunk index `refill`
+    // (when do_refill; past c_hi it is the next item's chunk, as in load_x)
     // goes out right there instead of after the whole chunk: half a chunk
     // more latency cover at no register cost.
     auto compute = [&](int p, int xp, int refill, auto do_refill) {
+      const bool cross = refill >= c_hi;
+      const int rc = !cross ? refill : (nvalid ? c_lo + (refill - c_hi) : c_hi - 1);
+      const __amdgpu_buffer_rsrc_t rres = cross && nvalid ? wres_n : wres;
+      const uint32_t rt0 = cross && nvalid ? tile0_n : tile0;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         bf16x8_t av[4];
         dequant_words(wq[p][nt], dq_scale(sc[p][nt]), kMaskLo, kMaskHi, kMagic, av);
         if constexpr (decltype(do_refill)::value) {
-          const uint32_t blk = tile0 + (uint32_t)(nt * a.n_chunks + refill) * kBlockBytes;
-          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wres, lane * 16, blk, kStreamAux);
+          const uint32_t blk = rt0 + (uint32_t)(nt * a.n_chunks + rc) * kBlockBytes;
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rres, lane * 16, blk, kStreamAux);
           wq[p][nt] = make_uint4(v[0], v[1], v[2], v[3]);
-          sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(wres, kBlockWeightBytes + lane * 2, blk, 0);
+          sc[p][nt] = __builtin_amdgcn_raw_buffer_load_b16(rres, kBlockWeightBytes + lane * 2, blk, 0);
           __builtin_amdgcn_sched_barrier(0);  // keep the refill where it is issued
         }
         // No liveness branch around the MFMA: a dead token tile multiplies
@@ -393,21 +438,24 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
 
     // PF is even, so chunk c_lo + i uses weight slot i % PF and token slot
     // i % 2, both compile-time inside the unrolled body.
-    // The steady-state body is straight-line: prefetch indices past the last
-    // chunk are clamped to it (a redundant, in-bounds load), so the compiler
-    // can count outstanding loads exactly instead of waiting for all of them.
+    // The steady-state body is straight-line: prefetch targets past the last
+    // chunk are the next item's first chunks (or the last chunk again, a
+    // redundant, in-bounds load), so the compiler can count outstanding
+    // loads exactly instead of waiting for all of them.
     static_assert(PF % 2 == 0, "even prefetch depth");
     if (c_lo < c_hi) {
       const int c_last = c_hi - 1;
-      load_x(0, c_lo);
+      if (!primed) {
+        load_x(0, c_lo);
 #pragma unroll
-      for (int p = 0; p < PF; ++p) load_w(p, min(c_lo + p, c_last));
+        for (int p = 0; p < PF; ++p) load_w(p, min(c_lo + p, c_last));
+      }
       int c = c_lo;
       for (; c + PF <= c_hi; c += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
-          load_x((p + 1) & 1, min(c + p + 1, c_last));
-          compute(p, p & 1, min(c + p + PF, c_last), std::true_type{});
+          load_x((p + 1) & 1, c + p + 1);
+          compute(p, p & 1, c + p + PF, std::true_type{});
         }
       }
 #pragma unroll
@@ -418,6 +466,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream(GemmArgs a) {
         }
       }
     }
+    primed = nvalid;  // chain holds: the main loop issued the next item's first chunks
 
     // Cross-wave K reduction: wave w finishes the (nt, mt) pairs with
     // (nt * MT + mt) % WK == w.
@@ -785,6 +834,8 @@ hipError_t launch_gemm(int kernel, int nt, int mt, int wk, int pf, const GemmArg
     CHORD_STREAM_MT(2, 1)
     CHORD_STREAM_CASE(1, 1, 8, 4)
     CHORD_STREAM_CASE(1, 1, 8, 8)
+    CHORD_STREAM_WK(1, 1, 2)
+    CHORD_STREAM_WK(1, 1, 4)
     CHORD_STREAM_WK(2, 1, 8)
     CHORD_STREAM_MT(2, 2)
     CHORD_STREAM_MT(4, 1)

@@ -141,6 +141,7 @@ struct GemmArgs {
   int tiles_per_item;    // 16-row weight tiles per work item
   int items_per_tile;    // n_tiles / tiles_per_item (tiled kernel: 256-row slices)
   int slices_per_item;   // tiled kernel, K <= 256: consecutive slices per work item
+  int no_chain;          // streaming kernel: 1 = every item restarts its load ring
   int tile_waves;        // tiled kernel, K > 256: waves per workgroup (4 or 8)
   float* partials;       // tiled kernel: K-split partial slots
   const TileDesc* split_tiles;  // tiled kernel: the split tiles (fixup pass)

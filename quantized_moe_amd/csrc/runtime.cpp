@@ -95,6 +95,7 @@ struct EnvOverrides {
   int prefetch = 0;
   int routed = 1;  // 0: routed indexed calls off (every indexed call reads the alignment)
   int fused = 1;   // 0: routed calls of a few tokens keep a separate combine launch
+  int stream_chain = 1;  // 0: streaming kernel restarts its load ring at every item
   bool log = false;
 };
 const EnvOverrides& env() {
@@ -112,6 +113,7 @@ const EnvOverrides& env() {
     if (const char* s = getenv("CHORD_W4A16_PREFETCH")) o.prefetch = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_ROUTED")) o.routed = atoi(s);
     if (const char* s = getenv("CHORD_W4A16_FUSED")) o.fused = atoi(s);
+    if (const char* s = getenv("CHORD_W4A16_STREAM_CHAIN")) o.stream_chain = atoi(s);
     if (const char* s = getenv("CHORD_LOG")) o.log = atoi(s) != 0;
     return o;
   }();
@@ -358,7 +360,7 @@ Plan make_plan(const PlanKey& key) {
     if (tok_e <= 4.0 && chunks >= 24 && N >= 2048) g.nt = 2;
     const int nt = ov_nt ? ov_nt : env_nt;
     const int wk = ov_wk ? ov_wk : env_wk;
-    if (nt == 2 || nt == 4) g.nt = nt;
+    if (nt == 1 || nt == 2 || nt == 4) g.nt = nt;
     if (wk == 1 || wk == 2 || wk == 4) g.wk = wk;
     if (ov_pf == 2 || ov_pf == 4) g.pf = ov_pf;
     if ((N / 16) % g.nt != 0) g.nt = 2;
@@ -607,6 +609,7 @@ hipError_t launch_planned(const Plan& plan, bool gate_up, GemmArgs g, TileDesc* 
   gs.tiles_per_item = sp.nt;
   gs.items_per_tile = sp.nt > 0 ? g.n_tiles / sp.nt : 0;
   gs.slices_per_item = sp.slices;
+  gs.no_chain = env().stream_chain == 0;
   if (sp.slices > 0) gs.items_per_tile = (gs.items_per_tile + sp.slices - 1) / sp.slices;
   gt.tiles = tiles_b;
   gt.tiles_per_item = kTileSlice / kTileRows;
