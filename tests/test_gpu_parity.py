@@ -180,6 +180,35 @@ def test_indexed_validate_flag_reports_bad_expert_ids():
     torch.cuda.synchronize()
 
 
+def test_streaming_ring_runs_on_across_items_and_skipped_tiles():
+    """More gate_up work items than the persistent grid holds (64 experts x 64
+    weight-tile groups), so each workgroup's load ring runs on from one item
+    into the next; one alignment block is corrupted in trusted mode, so a
+    workgroup meets a skipped item between two others and must restart its
+    ring there.  Every token without a slot in the corrupted block matches the
+    oracle, and the same call without the corruption matches it everywhere."""
+    banner("streaming ring across items, one skipped alignment block")
+    T, H, I, E, k = 64, 512, 2048, 64, 8
+    case = small_case(61, T, H, I, E, E, k)
+    x, ids, w, q13, s13, q2, s2, eb = case
+    ref = oracle.moe_layer(*case)
+    got, layer, al = run_indexed(*case, E_g=E, bm=16, override={"kernel": 1})
+    assert "gate_up nt=4 wk=1 pf=4" in C.last_plan(), C.last_plan()
+    check_close(got, ref, "all blocks")
+    s_ids, e_ids, ntpp = al
+    bad = 5
+    slots = host(s_ids)[bad * 16:(bad + 1) * 16]
+    hit = np.unique(slots[slots < T * k] // k)
+    e_ids[bad] = 999
+    out = layer.indexed(dev_bf16(x), dev(ids), dev(w), expert_begin=0, num_global_experts=E,
+                        align=(s_ids, e_ids, ntpp, 16), override={"kernel": 1})
+    torch.cuda.synchronize()
+    got2 = host_bf16(out)
+    keep = np.setdiff1d(np.arange(T), hit)
+    assert 0 < hit.size < T
+    check_close(got2[keep], ref[keep], "tokens outside the skipped block")
+
+
 @pytest.mark.parametrize("H,I,k", [(4224, 128, 2), (4096, 256, 1)])
 def test_single_token_deep_k_split(H, I, k):
     """One routed token on a deep-K gate_up: the planner takes one weight
