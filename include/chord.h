@@ -377,9 +377,9 @@ size_t chord_w4a16_moe_workspace_bytes(int mode, int T, int k, int E_l, int H, i
  *           may be NULL / 0, when chord_w4a16_moe_indexed_block_m returns 0
  *           for these shapes and no schedule override is given (a routed
  *           call: the gate_up launch builds each expert's row list from
- *           topk_ids in LDS; with T <= 16 and T*k <= 64 the down GEMM and
- *           the combine also run as one launch, summing w * y in fp32 without
- *           rounding y to bf16 first).
+ *           topk_ids in LDS; with T <= 16 and T*k <= 64, and no down
+ *           override, the down GEMM and the combine also run as one launch,
+ *           summing w * y in fp32 without rounding y to bf16 first).
  * out:      device bf16 [T, H]; every row is written (rows of tokens with no
  *           local expert are 0).
  * override: NULL or a schedule override.
