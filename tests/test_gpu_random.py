@@ -17,7 +17,11 @@ from tests.tolerance import check_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 16
+import os
+
+# Cases per sweep; CHORD_RANDOM_CASES widens them for a longer run.
+N_CASES = int(os.environ.get("CHORD_RANDOM_CASES", "16"))
+N_MASKED = max(12, N_CASES * 3 // 4)
 
 
 def setup_module(module):
@@ -64,6 +68,13 @@ def test_indexed_random_shapes(seed):
     assert C.last_plan() == C.chord_w4a16_moe_plan(
         C.MODE_INDEXED, c["T"], c["k"], c["E_g"], c["E_l"], c["H"], c["I"], c["bm"],
         sorted_ids.shape[0], num_cus=cus, override=override)
+    # A call the planner routes inside the GEMM gives the same output bit for
+    # bit without any alignment.
+    if override is None and C.chord_w4a16_moe_indexed_block_m(
+            c["T"], c["k"], c["E_g"], c["E_l"], c["H"], c["I"]) == 0:
+        assert "tiles=routed" in C.last_plan()
+        bare, _ = parity.run_routed(*case, E_g=c["E_g"])
+        assert np.array_equal(bare, got)
 
 
 def draw_masked_case(seed):
@@ -85,7 +96,7 @@ def draw_masked_case(seed):
                 pattern=pattern)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(N_MASKED))
 def test_masked_random_shapes(seed):
     from quantized_moe_amd import chord as C
     from quantized_moe_amd.moe import W4A16MoE
@@ -106,3 +117,39 @@ def test_masked_random_shapes(seed):
     for e in range(E):
         valid[e * max_m:e * max_m + int(mm[e])] = True
     check_close(got[valid], ref[valid], what=f"random masked case {seed}")
+
+
+def draw_routed_case(seed):
+    rng = np.random.Generator(np.random.PCG64(9000 + seed))
+    H = int(rng.choice([384, 512, 640, 1024]))
+    I = int(rng.choice([128, 256, 384, 512, 1024]))
+    E_g = int(rng.integers(4, 129))
+    E_l = int(rng.integers(1, E_g + 1))
+    eb = int(rng.integers(0, E_g - E_l + 1))
+    k = int(rng.integers(1, min(8, E_g) + 1))
+    T = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 257))]))
+    return dict(T=T, H=H, I=I, E_g=E_g, E_l=E_l, k=k, eb=eb)
+
+
+N_ROUTED = max(8, N_CASES // 2)
+
+
+@pytest.mark.parametrize("seed", range(N_ROUTED))
+def test_routed_random_shapes(seed):
+    """Calls the planner routes inside the GEMM, with no alignment at all:
+    within tolerance of the oracle; unless the down GEMM and the combine are
+    fused, bit for bit equal to the same schedule run on an alignment."""
+    C = parity.C
+    c = draw_routed_case(seed)
+    banner(f"random routed case {seed}: {c}")
+    if C.chord_w4a16_moe_indexed_block_m(c["T"], c["k"], c["E_g"], c["E_l"], c["H"], c["I"]):
+        pytest.skip("the planner does not route this shape")
+    case = small_case(3000 + seed, c["T"], c["H"], c["I"], c["E_g"], c["E_l"], c["k"], c["eb"])
+    got, layer = parity.run_routed(*case, E_g=c["E_g"])
+    plan = C.last_plan()
+    assert "tiles=routed" in plan, plan
+    check_close(got, oracle.moe_layer(*case), what=f"random routed case {seed}")
+    if "down+combine" not in plan:
+        aligned, _, _ = run_indexed(*case, E_g=c["E_g"], bm=16, layer=layer,
+                                    override={"kernel": 1})
+        assert np.array_equal(got, aligned)
