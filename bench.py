@@ -487,7 +487,7 @@ def main():
         copy_probe(args.copy_probe, args.steps)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N>1 is not supported "
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus N>1 is not supported "
                                    "(the layer takes one GPU's expert share, no collectives)"}))
         sys.exit(2)
     import torch
