@@ -328,8 +328,9 @@ chord_status chord_moe_combine(const chord_bf16* rows, int64_t n_rows, int H,
  * tokens, decide the schedule ([Novita] TL;DR and §"H200 Prefill und TP8").
  *
  * Returns 0 when the call needs no alignment: the planner routes it inside
- * the GEMM (the weight-streaming kernels at T*k <= 2048 slots, e.g. decode
- * and the small TP slices): every workgroup of the gate_up launch derives
+ * the GEMM (the weight-streaming kernels at T*k <= 2048 slots whose routing
+ * tables, (4 E_l + 2 + 2 T*k) ints, fit 32 KB of LDS, e.g. decode and the
+ * small TP slices): every workgroup of the gate_up launch derives
  * the rows of its expert from topk_ids itself, so the caller may skip
  * chord_moe_align and pass NULL alignment pointers (max_padded 0, block_m 0)
  * to chord_w4a16_moe_indexed.  This keeps the pages' contract of an indexed

@@ -175,6 +175,7 @@ constexpr int kFusedMaxTokens = 16;    // ... and T at most
 // first row, an end row, a first tile and a count; per slot a list entry and
 // at most one tile.
 inline size_t route_lds_bytes(int E, int n) { return (size_t)(4 * E + 2 + 2 * n) * sizeof(int); }
+constexpr size_t kRouteLdsMax = 32768;  // routed calls: table bytes at most (planner bound)
 
 struct CombineArgs {
   const uint16_t* rows;     // y [*, H] bf16

@@ -309,9 +309,12 @@ Plan make_plan(const PlanKey& key) {
   const int64_t slots = (int64_t)key.T * key.k;
   // The gate_up K must span more than 2 chunks: with K <= 256 the streaming
   // GEMM runs its short-K variant, which takes its tiles from the alignment.
+  // The routing tables share the launch's 64 KB of dynamic LDS with the K
+  // reduction area (at most 32 KB), so they get the other 32 KB: up to about
+  // a thousand local experts at the 2,048-slot maximum.
   p.routed = kernel == 1 && key.mode == kIndexed && key.ov[0] == 0 && env().kernel == 0 &&
              env().routed != 0 && slots >= 1 && slots <= kRoutedMaxSlots &&
-             key.H / kChunkK > 2;
+             key.H / kChunkK > 2 && route_lds_bytes(key.E_l, (int)slots) <= kRouteLdsMax;
 
   // Streaming GEMMs.
   const double tok_small = kernel == 3 ? std::min(tok_e, kSplitRows - 1) : tok_e;

@@ -148,3 +148,12 @@ def test_routed_calls_need_a_gate_up_k_over_two_chunks():
                                                        0, 0)
     assert "tiles=routed" in C.chord_w4a16_moe_plan(C.MODE_INDEXED, 256, 8, 384, 64, 384, 384, 0,
                                                    0)
+
+
+def test_routed_tables_fit_their_lds_share():
+    # The tables take (4 E + 2 + 2 n) ints of the launch's LDS, at most 32 KB:
+    # at 2,048 slots routed up to 1,022 local experts, aligned at the
+    # 1,024-expert limit; fewer slots leave room for every expert count.
+    assert C.chord_w4a16_moe_indexed_block_m(256, 8, 1022, 1022, 7168, 256) == 0
+    assert C.chord_w4a16_moe_indexed_block_m(256, 8, 1024, 1024, 7168, 256) != 0
+    assert C.chord_w4a16_moe_indexed_block_m(8, 8, 1024, 1024, 7168, 256) == 0
