@@ -209,6 +209,19 @@ def test_streaming_ring_runs_on_across_items_and_skipped_tiles():
     check_close(got2[keep], ref[keep], "tokens outside the skipped block")
 
 
+def test_streaming_ring_with_uneven_wave_ranges():
+    """A routed gate_up with 25 K chunks split over two waves (12 and 13
+    chunks) and more work items (44 experts x 64 weight-tile groups) than the
+    persistent grid holds: the wave with an even chunk count runs its load
+    ring on into the next item, the other restarts it, inside the same
+    workgroups; the layer matches the oracle."""
+    banner("streaming ring, uneven wave ranges, H=3200")
+    case = small_case(63, 48, 3200, 1024, 192, 48, 8)
+    got, _ = run_routed(*case, E_g=192)
+    assert "gate_up nt=2 wk=2 pf=2" in C.last_plan(), C.last_plan()
+    check_close(got, oracle.moe_layer(*case), "uneven wave ranges")
+
+
 @pytest.mark.parametrize("H,I,k", [(4224, 128, 2), (4096, 256, 1)])
 def test_single_token_deep_k_split(H, I, k):
     """One routed token on a deep-K gate_up: the planner takes one weight
